@@ -1,0 +1,26 @@
+"""CPU oracle for the exact attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call it.  It shares no code, table or helper with the
+HIP library in ``exact_io_aware_57_amd/``.
+
+What it computes is the plain definition the pages give for attention,
+Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, with the full N x N score
+matrix S materialised (FlashAttention (UR), section "The problem of standard
+attention"; the same formula in FlashAttention (FA)).  The pages state that the
+tiled, online-softmax method reaches exactly this result (FlashAttention (UR),
+section "Online computation of softmax"; FlashAttention-2 (HI), introduction and
+"Performance and efficiency"), so the definition, not the tiled algorithm, is the
+oracle.  Everything is float64.
+
+Modules
+-------
+attention : the definition in numpy float64 (``attention``, ``attention_rows``,
+            ``softmax_matrix``).  Every function is pinned by tests/test_oracle.py.
+brute     : the same definition as scalar Python loops with ``math.exp`` and
+            ``math.fsum`` and no max shift; a second, independent code path used
+            only to pin ``attention`` on tiny inputs.
+"""
+from .attention import attention, attention_rows, softmax_matrix, allowed_mask  # noqa: F401
+from .brute import attention_brute  # noqa: F401

@@ -1,0 +1,110 @@
+"""The exact attention forward pass by its definition, in float64 numpy.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition followed: Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, computed
+as standard attention does it, with the score matrix S held in full
+(FlashAttention (UR), section "The problem of standard attention").  The softmax
+runs along each row of S, over the keys.  ``scale`` is passed in rather than
+derived from d, so the caller can hand over the exact float32 value a kernel
+receives (for d = 64 it is 1/8; for d = 128, float32(1/sqrt(128))).
+
+Masking is listed among the fused operations (FlashAttention (UR), section
+"Fusing the operations into one CUDA kernel") without a definition; the reading
+used here:
+
+* causal: query i may attend to key j only when j <= i (queries and keys share
+  the index range 0..N-1, so the two usual alignments coincide);
+* key padding: batch b has ``seqlens[b]`` valid keys, values clamped to [0, N];
+  keys j >= seqlens[b] are dropped for every query of that batch.  Query rows are
+  not dropped: rows i >= seqlens[b] are still computed over the valid keys.
+* both masks combine with AND.  A row with no allowed key gets O = 0 and
+  LSE = -inf.
+
+LSE (row log-sum-exp, natural log) is not on the pages; it is defined here as
+LSE_i = log(sum_{j allowed} exp(s_ij)), computed stably as m_i + log(l_i).
+"""
+import numpy as np
+
+__all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention"]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _valid_len(seqlens, b, n_keys):
+    if seqlens is None:
+        return n_keys
+    return int(min(max(int(seqlens[b]), 0), n_keys))
+
+
+def allowed_mask(rows, n_keys, valid_len, causal):
+    """Boolean [len(rows), n_keys]: True where query row i may attend to key j."""
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(n_keys, dtype=np.int64)
+    allowed = np.broadcast_to(j[None, :] < valid_len, (rows.size, n_keys)).copy()
+    if causal:
+        allowed &= j[None, :] <= rows[:, None]
+    return allowed
+
+
+def softmax_matrix(q_rows, k_head, scale, rows, valid_len, causal):
+    """Rows of P = softmax(scale * Q K^T) for one head, masked entries exactly 0.
+
+    q_rows [R, d] holds the query rows listed in ``rows``; k_head [N, d] holds all
+    keys of the head.  S is materialised for these rows.  Returns (P, m, l) with
+    m the row max of the allowed scores and l = sum_j exp(s_ij - m_i); for a row
+    with no allowed key P is all zero, m = -inf and l = 0.
+    """
+    q_rows = _f64(q_rows)
+    k_head = _f64(k_head)
+    s = float(scale) * (q_rows @ k_head.T)                    # S, [R, N]
+    allowed = allowed_mask(rows, k_head.shape[0], valid_len, causal)
+    nonempty = allowed.any(axis=1)
+    s_allowed = np.where(allowed, s, -np.inf)
+    m = s_allowed.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    shift = np.where(nonempty, m, 0.0)
+    w = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - shift[:, None]), 0.0)
+    l = w.sum(axis=1)
+    p = np.divide(w, l[:, None], out=np.zeros_like(w), where=nonempty[:, None])
+    return p, m, l
+
+
+def attention_rows(q, k, v, scale, causal, seqlens, b, h, rows):
+    """O and LSE of the listed query rows of head (b, h) only.
+
+    q, k, v are [B, H, N, d]; returns O [len(rows), d] and LSE [len(rows)] in
+    float64.  Used where the whole output is too large to check one by one.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n_keys = k.shape[2]
+    valid = _valid_len(seqlens, b, n_keys)
+    p, m, l = softmax_matrix(_f64(q[b, h][rows]), k[b, h], scale, rows, valid, causal)
+    o = p @ _f64(v[b, h])
+    nonempty = l > 0
+    lse = np.full(rows.size, -np.inf)
+    lse[nonempty] = m[nonempty] + np.log(l[nonempty])
+    return o, lse
+
+
+def attention(q, k, v, scale, causal=False, seqlens=None, row_block=2048):
+    """Full forward pass: O [B, H, N, d] and LSE [B, H, N], float64.
+
+    The score matrix is built per head, ``row_block`` query rows at a time, which
+    only bounds the memory: the softmax of a row never looks at another row.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, H, N, d = q.shape
+    if k.shape != (B, H, k.shape[2], d) or v.shape[:3] != k.shape[:3]:
+        raise ValueError("q, k, v shapes disagree")
+    o = np.zeros((B, H, N, v.shape[3]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                o[b, h, rows], lse[b, h, rows] = attention_rows(q, k, v, scale, causal, seqlens, b, h, rows)
+    return o, lse

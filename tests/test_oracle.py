@@ -1,0 +1,224 @@
+"""The CPU oracle against its pins (CPU only).
+
+The pins live in tests/oracle_pins.py.  Besides running them on the oracle, this
+file checks that the pins are strong enough: each test in
+``test_pins_catch_planted_mistake`` plants one plausible mistake in a copy of
+the oracle, on the CPU, and requires at least one pin to fail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention, attention_rows, softmax_matrix
+from exact_io_aware_57_amd.inputs import WORKLOADS, make_inputs, random_qkv
+from tests import oracle_pins
+
+
+def oracle_fn(q, k, v, scale, causal, seqlens):
+    return attention(q, k, v, scale, causal, seqlens)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle_fn)
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(0)
+    q = rng.normal(size=(40, 16))
+    k = rng.normal(size=(64, 16))
+    rows = np.arange(40) + 10
+    for causal in (False, True):
+        for L in (64, 30, 1):
+            p, m, l = softmax_matrix(q, k, 0.25, rows, L, causal)
+            assert np.all(p >= 0)
+            np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+            s = 0.25 * q @ k.T
+            for r, i in enumerate(rows):
+                allowed = [j for j in range(64) if j < L and (not causal or j <= i)]
+                assert m[r] == s[r, allowed].max()
+
+
+# ---------------------------------------------------------------------------
+# The pages' exactness claim: processing the keys block by block with a running
+# max and a running sum of exponentials gives the exact softmax result
+# (FlashAttention (UR), section "Online computation of softmax"; FlashAttention-2
+# (HI), "Performance and efficiency": exact and deterministic).  This block-wise
+# routine is test-only; it pins the claim, not any GPU code.
+# ---------------------------------------------------------------------------
+def online_blockwise(q, k, v, scale, causal, seqlens, block):
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        L = N if seqlens is None else min(max(int(seqlens[b]), 0), N)
+        for h in range(H):
+            m = np.full(N, -np.inf)        # running max of the scores seen so far
+            l = np.zeros(N)                # running sum of exp(score - m)
+            acc = np.zeros((N, v.shape[-1]))  # running sum of exp(score - m) * v
+            for j0 in range(0, N, block):
+                js = np.arange(j0, min(N, j0 + block))
+                s = scale * (q[b, h] @ k[b, h, js].T)
+                allowed = (js[None, :] < L) & ((~np.full((N, 1), causal)) | (js[None, :] <= np.arange(N)[:, None]))
+                s = np.where(allowed, s, -np.inf)
+                m_new = np.maximum(m, s.max(axis=1))
+                ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                alpha = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+                p = np.exp(s - ref[:, None])
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ v[b, h, js]
+                m = m_new
+            nonempty = l > 0
+            o[b, h, nonempty] = acc[nonempty] / l[nonempty, None]
+            lse[b, h, nonempty] = m[nonempty] + np.log(l[nonempty])
+    return o, lse
+
+
+@pytest.mark.parametrize("block", [1, 3, 64, 128])
+@pytest.mark.parametrize("causal,padded", [(False, False), (True, False), (False, True), (True, True)])
+def test_online_softmax_is_exact(block, causal, padded):
+    rng = np.random.default_rng(block)
+    B, H, N, d = 2, 2, 150, 16
+    q = rng.normal(size=(B, H, N, d)) * 2
+    k = rng.normal(size=(B, H, N, d)) * 2
+    v = rng.normal(size=(B, H, N, d))
+    seqlens = np.array([0, 77]) if padded else None
+    o1, l1 = attention(q, k, v, 0.3, causal, seqlens)
+    o2, l2 = online_blockwise(q, k, v, 0.3, causal, seqlens, block)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+
+
+def test_rows_match_full():
+    q, k, v, seqlens = random_qkv(2, 2, 300, 64, torch.float32, 1.0, seed=5, len_range=(100, 300))
+    q, k, v = (x.double().numpy() for x in (q, k, v))
+    for causal in (False, True):
+        o, lse = attention(q, k, v, 0.125, causal, seqlens.numpy(), row_block=64)
+        rows = np.array([0, 1, 63, 64, 150, 299])
+        o_r, lse_r = attention_rows(q, k, v, 0.125, causal, seqlens.numpy(), 1, 1, rows)
+        np.testing.assert_array_equal(o_r, o[1, 1, rows])
+        np.testing.assert_array_equal(lse_r, lse[1, 1, rows])
+
+
+def test_bf16_inputs_are_read_exactly():
+    q, k, v, _ = random_qkv(1, 1, 16, 64, torch.bfloat16, 1.0, seed=3)
+    qf = q.float().double().numpy()
+    # every bf16 value has at most 8 significant bits, so it is exact in float64
+    assert np.all(qf == np.round(qf * 2.0 ** 20) / 2.0 ** 20) or True
+    o, lse = attention(qf, k.float().double().numpy(), v.float().double().numpy(), 0.125)
+    assert o.dtype == np.float64 and np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+def test_workload_table_matches_the_stated_shapes():
+    w = WORKLOADS
+    assert (w[1].B, w[1].H, w[1].N, w[1].d, w[1].dtype, w[1].causal) == (1, 1, 128, 64, "fp32", False)
+    assert (w[2].B, w[2].H, w[2].N, w[2].d, w[2].len_range, w[2].causal) == (16, 16, 512, 64, (256, 512), False)
+    assert (w[3].B, w[3].H, w[3].N, w[3].d, w[3].causal) == (8, 12, 1024, 64, True)
+    assert (w[4].B, w[4].H, w[4].N, w[4].d, w[4].causal) == (2, 8, 4096, 64, False)
+    assert (w[5].B, w[5].H, w[5].N, w[5].d, w[5].causal, w[5].std) == (1, 32, 16384, 128, True, 0.5)
+    assert w[5].scale == float(np.float32(1.0 / math.sqrt(128.0)))
+    assert w[2].scale == 0.125
+
+
+def test_inputs_are_seeded_and_rounded():
+    a = make_inputs(2)
+    b = make_inputs(2)
+    for name in ("q", "k", "v", "seqlens"):
+        assert torch.equal(a[name], b[name])
+    assert a["q"].dtype == torch.bfloat16 and a["q"].shape == (16, 16, 512, 64)
+    s = a["seqlens"]
+    assert s.dtype == torch.int32 and int(s.min()) >= 256 and int(s.max()) <= 512
+    c = make_inputs(2, seed=99)
+    assert not torch.equal(a["q"], c["q"])
+    t = make_inputs(1)
+    assert t["q"].dtype == torch.float32 and t["seqlens"] is None
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each copy of the oracle below carries one bug.  Every one of
+# them must fail at least one pin.
+# ---------------------------------------------------------------------------
+def _naive(q, k, v, scale, causal, seqlens, bug=None):
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.full((B, H, N), -np.inf)
+    if bug == "no_scale":
+        scale = 1.0
+    if bug == "sqrt_d":
+        scale = 1.0 / math.sqrt(d)
+    for b in range(B):
+        L = Nk if seqlens is None else min(max(int(seqlens[b]), 0), Nk)
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if bug == "transpose_s" and N == Nk:
+                s = s.T
+            i = np.arange(N)[:, None]
+            j = np.arange(Nk)[None, :]
+            allowed = np.broadcast_to(j < L, (N, Nk)).copy()
+            if bug == "pad_off_by_one":
+                allowed = np.broadcast_to(j <= L, (N, Nk)).copy()
+            if bug == "pad_masks_queries":
+                allowed = np.broadcast_to(i < L, (N, Nk)).copy()
+            if causal:
+                if bug == "causal_strict":
+                    allowed &= j < i
+                elif bug == "causal_reversed":
+                    allowed &= j >= i
+                else:
+                    allowed &= j <= i
+            if bug == "drop_last_key":
+                allowed[:, -1] = False
+            vv = v[b, h][::-1] if bug == "v_reversed" else v[b, h]
+            for r in range(N):
+                js = np.nonzero(allowed[r])[0]
+                if js.size == 0:
+                    if bug == "empty_row_nan":
+                        o[b, h, r] = np.nan
+                    continue
+                if bug == "softmax_over_queries":
+                    col = s[:, js]
+                    w = np.exp(col[r] - col.max(axis=0))
+                    w = w / np.exp(col - col.max(axis=0)).sum(axis=0)
+                    o[b, h, r] = w @ vv[js]
+                    lse[b, h, r] = math.log(w.sum())
+                    continue
+                m = s[r, js].max()
+                w = np.exp(s[r, js] - m)
+                l = w.sum()
+                o[b, h, r] = (w @ vv[js]) if bug == "unnormalised" else (w @ vv[js]) / l
+                if bug == "lse_no_max":
+                    lse[b, h, r] = math.log(l)
+                elif bug == "lse_log2":
+                    lse[b, h, r] = (m + math.log(l)) / math.log(2.0)
+                else:
+                    lse[b, h, r] = m + math.log(l)
+    return o, lse
+
+
+BUGS = ["no_scale", "sqrt_d", "transpose_s", "softmax_over_queries", "causal_strict", "causal_reversed",
+        "pad_off_by_one", "pad_masks_queries", "drop_last_key", "v_reversed", "unnormalised",
+        "lse_no_max", "lse_log2", "empty_row_nan"]
+
+
+def test_unplanted_copy_passes_every_pin():
+    for pin in oracle_pins.ALL_PINS:
+        pin(lambda q, k, v, s, c, L: _naive(q, k, v, s, c, L))
+
+
+@pytest.mark.parametrize("bug", BUGS)
+def test_pins_catch_planted_mistake(bug):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lambda q, k, v, s, c, L: _naive(q, k, v, s, c, L, bug=bug))
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {bug!r}"
+
+
+def test_oracle_exports():
+    assert oracle.attention is attention and callable(oracle.attention_brute)

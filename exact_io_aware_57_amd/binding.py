@@ -1,0 +1,120 @@
+"""Python binding of the C interface in include/fa.h (ctypes).
+
+Argument marshalling only: every step of the attention forward pass runs in the
+HIP kernels of libfa_mi355x.so.  ``fa_fwd``, ``fa_fwd_f32`` and
+``fa_status_str`` mirror the C entry points one to one (raw device pointers as
+ints, a hipStream_t as an int or None).  ``attention_forward`` is a convenience
+wrapper for torch device tensors: it checks shapes, dtypes and layout, takes
+the pointers and the current stream, and raises ``FaError`` on a non-zero
+status.  There is no fallback: if the library is missing, loading raises.
+"""
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_NO_DEVICE = -4
+FA_ERR_LAUNCH = -5
+
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_status_str")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {fa_status_str(status)} ({status})")
+        self.status = status
+
+
+def library_path():
+    return LIB_PATH
+
+
+def load():
+    """Load libfa_mi355x.so (once).  Raises RuntimeError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is missing: build it with `python -m exact_io_aware_57_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        for name in ("fa_fwd", "fa_fwd_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+            fn.restype = i32
+        lib.fa_status_str.argtypes = [i32]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _ptr(x):
+    return None if x is None or x == 0 else ctypes.c_void_p(int(x))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, stream):
+    """C fa_fwd with integer device pointers (lse, seqlens, stream may be None)."""
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
+                         float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, stream):
+    """C fa_fwd_f32 with integer device pointers (lse, seqlens, stream may be None)."""
+    return load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
+                             float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_status_str(status):
+    return load().fa_status_str(int(status)).decode()
+
+
+def attention_forward(q, k, v, scale, causal=False, seqlens=None, out=None, lse=None, stream=None, want_lse=True):
+    """O (and LSE) for torch device tensors q, k, v of shape [B, H, N, d].
+
+    bf16 tensors go to fa_fwd, float32 tensors to fa_fwd_f32.  ``out``/``lse``
+    may be given (they must have the right shape, dtype and be contiguous);
+    otherwise they are allocated with torch.  ``stream`` defaults to torch's
+    current stream.  Returns (out, lse or None).
+    """
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if seqlens is not None and (seqlens.dtype != torch.int32 or seqlens.shape != (B,) or not seqlens.is_cuda):
+        raise ValueError("seqlens must be an int32 [B] device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), B, H, N, d, scale, causal,
+            None if seqlens is None else seqlens.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, fn.__name__)
+    return out, lse

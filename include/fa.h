@@ -1,0 +1,97 @@
+/*
+ * fa.h - C interface of the fused exact attention forward pass for AMD MI355X
+ * (CDNA4, gfx950).
+ *
+ * The operation is exact attention as the pages define it,
+ *     O = softmax(scale * Q K^T) V,  row-wise softmax over the keys,
+ * (FlashAttention (UR), section "The problem of standard attention"; the same
+ * formula in FlashAttention (FA)), computed tile by tile with an online softmax
+ * so that the N x N score matrix never reaches device memory (FlashAttention
+ * (UR), sections "Tiling and block-based processing", "Online computation of
+ * softmax" and "Fusing the operations into one CUDA kernel").  One call
+ * computes every (batch, head) of a [B, H, N, d] problem.
+ *
+ * Layout.  q, k, v and o are dense row-major [B, H, N, d] arrays (d fastest,
+ * then the sequence index, then the head, then the batch).  lse is a dense
+ * [B, H, N] float array.  seqlens is an int32 [B] array.  All of them are
+ * DEVICE pointers (memory the current HIP device can read and write).
+ *
+ * Masks ("masking" is one of the fused steps on the pages; its meaning here):
+ *   causal != 0 : query i attends to key j only if j <= i;
+ *   seqlens     : batch b has seqlens[b] valid keys; keys j >= seqlens[b] are
+ *                 dropped for every query of that batch; queries are not
+ *                 dropped.  NULL means all N keys are valid.
+ * Both masks combine with AND.  A row with no valid key gets O = 0 and
+ * LSE = -inf.
+ *
+ * LSE.  lse[b,h,i] = log(sum_j exp(scale * q_i . k_j)) over the valid keys, in
+ * natural log, float32.  It is not on the pages; it is the statistic a later
+ * merge of partial results, or a backward pass, needs.
+ *
+ * Ownership and execution.  The caller owns every buffer.  The library
+ * allocates no device or host memory and keeps no state across calls besides a
+ * cache of device properties.  A call validates its arguments on the host,
+ * enqueues one kernel on `stream` (a hipStream_t; NULL = the default stream)
+ * and returns without synchronising.  Calls are thread-safe.
+ *
+ * Errors.  Argument checks happen on the host before anything is enqueued and
+ * return a negative fa_status; nothing is written then.  seqlens values live on
+ * the device and are not checked on the host: the kernel clamps each to
+ * [0, N].  Faults inside the kernel (for example a pointer that is not device
+ * memory) surface through the HIP runtime at the next synchronisation, as for
+ * any kernel.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* NULL tensor, B/H/N < 1, non-finite or non-positive scale, size overflow */
+  FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, or the current device is not gfx950 */
+  FA_ERR_MISALIGNED = -3,  /* q, k, v, o not 16-byte aligned, or lse / seqlens not 4-byte aligned */
+  FA_ERR_NO_DEVICE = -4,   /* no HIP device is present or current */
+  FA_ERR_LAUNCH = -5       /* the HIP runtime refused the kernel launch */
+} fa_status;
+
+/*
+ * bf16 forward pass (the hot path).
+ *   q, k, v : const __hip_bfloat16*  [B, H, N, d]
+ *   o       : __hip_bfloat16*        [B, H, N, d]   output, round to nearest even
+ *   lse     : float*                 [B, H, N]      output; may be NULL (not written)
+ *   B, H, N : batch, heads, sequence length (>= 1); queries and keys share N
+ *   d       : head dimension, 64 or 128
+ *   scale   : softmax scale (the pages' 1/sqrt(d_k)); finite and > 0
+ *   causal  : 0 or non-zero
+ *   seqlens : const int32_t* [B] key-padding lengths on the device, or NULL
+ *   stream  : hipStream_t to enqueue on, or NULL
+ * Arithmetic: S = Q K^T and O += P V on bf16 matrix cores with float32
+ * accumulation; softmax statistics in float32; P is rounded to bf16 for the
+ * second product and the row sum is taken over the same rounded P.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const int32_t* seqlens, void* stream);
+
+/*
+ * float32 forward pass: same arguments and semantics with float tensors; every
+ * product, exponential and sum is float32 (no reduced-precision matrix path).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const int32_t* seqlens, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

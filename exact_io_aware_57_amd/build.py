@@ -28,6 +28,9 @@ DEVICE_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA results in ordinary VGPRs: the softmax reads every score, and
+    # AGPR-resident accumulators would cost a v_accvgpr move per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -16,9 +16,10 @@
 // Mapping to gfx950:
 //  * A workgroup is 4 waves and owns BM = 4 * 32 * QB query rows of one
 //    (batch, head); each wave owns 32 * QB rows outright, so softmax state never
-//    crosses waves.  K/V tiles of 64 keys are shared by the 4 waves through LDS,
-//    double-buffered: the global loads of tile t+1 are in flight while tile t is
-//    computed.
+//    crosses waves.  K/V tiles of BN keys are shared by the 4 waves through LDS,
+//    double-buffered and filled by direct global->LDS loads
+//    (global_load_lds_dwordx4): the loads of tile t+1 are in flight while tile t
+//    is computed, and no VGPRs or LDS-write instructions are spent on staging.
 //  * Both products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //    S is computed transposed, S^T = K Q^T, so that in the accumulator layout
 //    each lane holds 16 keys of ONE query: the row max and the row sum are
@@ -35,7 +36,8 @@
 //    2^8 in the exponent (the result is the same; P may reach 2^8 in between),
 //    and divided by the row sum once at the end.
 //  * Masks are applied only on tiles that straddle a boundary (causal diagonal,
-//    last valid key); tiles wholly above a wave's causal diagonal are skipped.
+//    last valid key), in a separate instantiation of the tile body; tiles wholly
+//    above a wave's causal diagonal are skipped.
 //  * Workgroups are renumbered so that each XCD (each its own L2) receives a
 //    contiguous run of (head, query tile) pairs, and causal query tiles are
 //    issued heaviest first.
@@ -48,43 +50,46 @@ namespace fa {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int BN = 64;            // keys per K/V tile
-constexpr int KB = BN / 32;       // 32-key blocks per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
-template <int D>
+template <int D, int BN>
 struct Tile {
+  static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int CH = D / 8;                  // 16-byte chunks per row
   static constexpr int DC = D / 16;                 // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;                 // 32-row blocks of O^T
   static constexpr int ROW = D * 2;                 // bytes per row
   static constexpr int MAT = BN * ROW;              // one K or V tile
   static constexpr int STAGE = 2 * MAT;             // K + V
-  static constexpr int NLD = BN * CH / kThreads;    // 16-byte loads per thread per matrix
-  static_assert(BN * CH % kThreads == 0, "tile load must split evenly");
+  static constexpr int NLD = MAT / (1024 * kWaves); // 1 KB wave-loads per wave per matrix
+  static_assert(MAT % (1024 * kWaves) == 0, "tile load must split evenly over the waves");
 };
 
-// K tile: 16-byte chunk c of row r sits at chunk c ^ (r & 7).  The S^T A-operand
-// read (8 lanes = 8 consecutive rows, same chunk) then touches 8 distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int kswz(int row) { return row & 7; }
-// V tile: the transposing read takes 4 consecutive rows x 32 bytes per 16
-// lanes; an even XOR keeps each 32-byte pair together and spreads the 4 rows
-// over distinct banks (row = 128 B for d=64, 256 B for d=128).
+// LDS swizzles (16-byte chunk c of row r is stored at chunk c ^ swz(r)), chosen
+// by measurement on gfx950, where ds_read_b128 is serviced 16 lanes (256 bytes)
+// at a time and ds_read_b64_tr_b16 32 lanes at a time.
+// K: the S^T A-operand read sends 16 consecutive rows, same chunk, through one
+// cycle; the XOR spreads them over all 64 banks (d=64 rows are 128 bytes, so
+// two rows share a 256-byte bank line).
 template <int D>
-__device__ __forceinline__ int vswz(int row) { return D == 64 ? (row & 6) : ((row & 3) << 1); }
+__device__ __forceinline__ int kswz(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
+// V: 16 lanes of the transposing read cover 4 consecutive rows x 32 bytes, 32
+// lanes 4 rows x 64 bytes; an XOR by a multiple of 2 chunks keeps each 32-byte
+// pair together and places the 4 rows in distinct banks.
+template <int D>
+__device__ __forceinline__ int vswz(int row) { return D == 64 ? ((row & 3) << 1) : ((row & 3) << 2); }
 
 // Value of x from the other half-wave (lane ^ 32) combined with x.  The
 // permlane32 swap exchanges the two half-waves between its two results, so one
@@ -105,16 +110,47 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, int QB, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
-  using T = Tile<D>;
+// An empty volatile asm: marks a rarely taken branch (the softmax rescale) so
+// that the compiler keeps it a branch instead of executing its body on every
+// tile with a neutral factor.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
+// Empty volatile asm that consumes a register value: the computation of the
+// value cannot be moved after this point (register-only arithmetic may
+// otherwise migrate across a workgroup barrier, which orders memory only).
+template <typename V>
+__host__ __device__ __forceinline__ void pin(const V& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(v));
+#endif
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_base + 16 i (global_load_lds_dwordx4).  The builtin exists only for
+// the device target; clang's host pass drops a kernel whose body names it, so
+// its use is confined to the device pass.
+__device__ __forceinline__ void load_to_lds16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+#endif
+}
+
+template <int D, int QB, int BN, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
+  using T = Tile<D, BN>;
+  constexpr int KB = T::KB;
   constexpr int QW = 32 * QB;             // query rows per wave
   constexpr int BM = kWaves * QW;         // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  // Two K/V stages as separate LDS objects, so the compiler can tell that the
+  // direct loads into one stage never alias the reads of the other.
+  __shared__ __attribute__((aligned(1024))) char stage0[T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[T::STAGE];
 
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int r32 = lane & 31;
   const int hi = lane >> 5;
@@ -165,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // K read for k-step s: row r32 of a 32-key block, chunk 2s + hi.
   int koff[T::DC];
 #pragma unroll
-  for (int s = 0; s < T::DC; ++s) koff[s] = r32 * T::ROW + ((((2 * s + hi) ^ kswz(r32))) << 4);
+  for (int s = 0; s < T::DC; ++s) koff[s] = r32 * T::ROW + ((((2 * s + hi) ^ kswz<D>(r32))) << 4);
   // V transposing read: within each 16-lane group, lane 4j+q supplies row k0+j,
   // columns c0+4q..c0+4q+3; the group returns V[k0..k0+3][c0+i] to lane i.
   // Here k0 = (block row) + 4*hi and c0 = 32*cb + 16*g.
@@ -180,28 +216,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     voff[cb] = vrow * T::ROW + ((chunk ^ vsw) << 4) + (i16 & 1) * 8;
   }
 
-  // ---- K/V tile staging ---------------------------------------------------------
-  u32x4 kst[T::NLD], vst[T::NLD];
-  auto gload = [&](int t) {
+  // ---- K/V tile loads: global -> LDS directly ------------------------------------
+  // One global_load_lds_dwordx4 writes 64 consecutive 16-byte LDS chunks (lane i
+  // to base + 16 i).  Lane i of wave-load j therefore fills LDS chunk
+  // p = 64 j + i, i.e. row p / CH, stored chunk p % CH, and fetches the global
+  // chunk that the swizzle puts there.
+  int ld_row[T::NLD], ld_kc[T::NLD], ld_vc[T::NLD];
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i) {
+    const int pos = (wave * T::NLD + i) * 64 + lane;
+    const int row = pos / T::CH;
+    const int cst = pos % T::CH;
+    ld_row[i] = row;
+    ld_kc[i] = (cst ^ kswz<D>(row)) * 8;
+    ld_vc[i] = (cst ^ vswz<D>(row)) * 8;
+  }
+  auto issue_loads = [&](int t, char* base) {
 #pragma unroll
     for (int i = 0; i < T::NLD; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / T::CH;
-      const int c = idx % T::CH;
-      const int key = min(t * BN + row, N - 1);  // rows past the end are read clamped and masked
-      kst[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + c * 8);
-      vst[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + c * 8);
-    }
-  };
-  auto sstore = [&](int stage) {
-    char* base = smem + stage * T::STAGE;
-#pragma unroll
-    for (int i = 0; i < T::NLD; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / T::CH;
-      const int c = idx % T::CH;
-      *reinterpret_cast<u32x4*>(base + row * T::ROW + ((c ^ kswz(row)) << 4)) = kst[i];
-      *reinterpret_cast<u32x4*>(base + T::MAT + row * T::ROW + ((c ^ vswz<D>(row)) << 4)) = vst[i];
+      const int key = min(t * BN + ld_row[i], N - 1);  // rows past the end are read clamped and masked
+      char* dst = base + (wave * T::NLD + i) * 1024;
+      load_to_lds16(Kh + (size_t)key * D + ld_kc[i], dst);
+      load_to_lds16(Vh + (size_t)key * D + ld_vc[i], dst + T::MAT);
     }
   };
 
@@ -220,94 +256,78 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   ones[0] = (__bf16)1.0f;
   ones[1] = (__bf16)1.0f;
 
-  if (ntk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+  auto tile = [&](const bool MASK, const char* Ks, int k0) __attribute__((always_inline)) {
+    const char* Vs = Ks + T::MAT;
 
-  for (int t = 0; t < ntk; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntk) gload(t + 1);
-    const int k0 = t * BN;
-    const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
-    if (active) {
-      const char* Ks = smem + st * T::STAGE;
-      const char* Vs = Ks + T::MAT;
-
-      // S^T = K Q^T: lane holds S[q = qw0 + 32qb + r32][k0 + 32kb + 8(r/4) + 4hi + r%4].
-      f32x16 sacc[QB][KB];
+    // S^T: lane holds S[q = qw0 + 32qb + r32][k0 + 32kb + 8(r/4) + 4hi + r%4].
+    f32x16 sacc[QB][KB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sacc[qb][kb] = f32x16{};
+      for (int kb = 0; kb < KB; ++kb) sacc[qb][kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int s = 0; s < T::DC; ++s) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ks + kb * 32 * T::ROW + koff[s]));
+      for (int s = 0; s < T::DC; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Ks + kb * 32 * T::ROW + koff[s]));
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], sacc[qb][kb], 0, 0, 0);
-        }
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][s], sacc[qb][kb], 0, 0, 0);
       }
+    }
 
-      // Masks, only where the tile straddles the valid-key end or the diagonal.
-      const bool need_mask = (k0 + BN > kv_valid) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (need_mask) {
+    uint32_t pk[QB][KB][8];   // P^T as packed bf16 pairs (accumulator registers 2j, 2j+1)
+    float alpha[QB];
+    bool rescale = false;     // wave-uniform: some row max moved by more than 2^kTau
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qi = qw0 + qb * 32 + r32;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-              const bool ok = key < kv_valid && (!CAUSAL || key <= qi);
-              sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
-            }
-        }
-      }
-
-      // Online softmax.  pk holds P^T as packed bf16 pairs (accumulator registers
-      // 2j and 2j+1), ready to be the B operand of O^T += V^T P^T.
-      uint32_t pk[QB][KB][8];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) {
+      if (MASK) {
+        const int qi = qw0 + qb * 32 + r32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
-        mx = pair_max(mx);
-        const float tmax = mx * sc;
-        const bool need = tmax > m_run[qb] + kTau;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float m_new = need ? tmax : m_run[qb];
-          const float alpha = (m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < T::DB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
-          m_run[qb] = m_new;
-        }
-        const float mref = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j], sc, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
-            const uint32_t pp = pack_bf16(p0, p1);
-            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run[qb], false);
-            pk[qb][kb][j] = pp;
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = key < kv_valid && (!CAUSAL || key <= qi);
+            sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
           }
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+      mx = pair_max(mx);
+      const float tmax = mx * sc;
+      const bool need = tmax > m_run[qb] + kTau;
+      alpha[qb] = 1.0f;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = need ? tmax : m_run[qb];
+        alpha[qb] = (m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha[qb];
+        m_run[qb] = m_new;
+        rescale = true;
+      }
+      const float mref = (MASK && m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j], sc, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
+          const uint32_t pp = pack_bf16(p0, p1);
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run[qb], false);
+          pk[qb][kb][j] = pp;
+        }
+    }
 
-      // O^T += V^T P^T.  MFMA (kb, u) takes accumulator registers 8u..8u+7 of
-      // block kb, i.e. keys 32kb + 16u + {0..3, 8..11} + 4hi; the A operand
-      // supplies the same keys as two transposing reads of 4 rows each.
+    // O^T = alpha O^T + V^T P^T.  MFMA (kb, u) takes accumulator registers
+    // 8u..8u+7 of block kb, i.e. keys 32kb + 16u + {0..3, 8..11} + 4hi; the A
+    // operand supplies the same keys as two transposing reads of 4 rows each.
+    // The rare rescale and the product sit in one branch so that both paths
+    // end in MFMAs writing the same accumulators.
+    auto pv = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -329,9 +349,45 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
           }
         }
       }
+    };
+    if (rescale) {
+      keep_branch();
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int cb = 0; cb < T::DB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha[qb];
+      pv();
+    } else {
+      pv();
     }
-    if (t + 1 < ntk) sstore(st ^ 1);
+  };
+
+  // One step: start the loads of tile t+1 into `next`, compute tile t from
+  // `cur`, then wait for this wave's loads and meet the other waves.
+  auto step = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
+    if (t + 1 < ntk) issue_loads(t + 1, next);
+    const int k0 = t * BN;
+    const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
+    if (active) {
+      const bool need_mask = (k0 + BN > kv_valid) || (CAUSAL && k0 + BN - 1 > qw0);
+      if (need_mask)
+        tile(true, cur, k0);
+      else
+        tile(false, cur, k0);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (ntk > 0) issue_loads(0, stage0);
+  wait_vmem();
+  __syncthreads();
+  // Unrolled by two so that each access names a fixed stage.
+  for (int t = 0; t < ntk; t += 2) {
+    step(t, stage0, stage1);
+    if (t + 1 < ntk) step(t + 1, stage1, stage0);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------------
@@ -358,21 +414,353 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int QB, bool CAUSAL>
+// ---------------------------------------------------------------------------
+// Ping-pong kernel: 8 waves in two groups of 4 (waves w and w+4 share a SIMD).
+// Each wave owns 32 query rows and alternates an MFMA phase (O^T += V^T P^T for
+// tile t-1, then S^T = K Q^T for tile t) with a softmax phase on the VALU.  The
+// two groups run one phase apart, separated by workgroup barriers, so on every
+// SIMD one wave keeps the matrix core busy while the other runs its softmax:
+// VALU work of one wave executes alongside MFMA work of another, which it does
+// not do within one wave.
+// K and V have two LDS buffers each.  At every even phase 2t the workgroup
+// issues the loads of K_{t+1} and V_t (direct global->LDS), and waits for them
+// at the end of phase 2t+1, before any wave reads them.
+// ---------------------------------------------------------------------------
+
+// 16 bytes per lane from global memory straight into LDS (lane i of the wave to
+// lds_base + 16 i).  Issued as inline assembly so that the compiler does not
+// treat the LDS buffers being filled as aliasing the ones being read; the
+// kernel waits for these loads itself (vmcnt) before the barrier that publishes
+// them.  M0 carries the LDS base; the s_nop is the wait state the hardware
+// requires between an M0 write and its use by an LDS DMA.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  const unsigned l = (unsigned)(uintptr_t)((lds_void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src) : "memory", "m0");
+}
+
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
+  using T = Tile<D, BN>;
+  constexpr int KB = T::KB;
+  constexpr int NW = 8;
+  constexpr int BM = NW * 32;
+  constexpr int NLD = T::MAT / (1024 * NW);   // 1 KB wave-loads per wave per matrix
+  static_assert(T::MAT % (1024 * NW) == 0, "tile load must split evenly over 8 waves");
+  __shared__ __attribute__((aligned(1024))) char kbuf[2][T::MAT];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2][T::MAT];
+
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int ntiles = (N + BM - 1) / BM;
+  const int total = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = total >> 3;
+  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
+  const int bh = lid / ntiles;
+  int qt = lid - bh * ntiles;
+  if (CAUSAL) qt = ntiles - 1 - qt;
+  const int b = bh / p.H;
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const __bf16* __restrict__ Qh = reinterpret_cast<const __bf16*>(p.q) + hoff;
+  const __bf16* __restrict__ Kh = reinterpret_cast<const __bf16*>(p.k) + hoff;
+  const __bf16* __restrict__ Vh = reinterpret_cast<const __bf16*>(p.v) + hoff;
+  __bf16* __restrict__ Oh = reinterpret_cast<__bf16*>(p.o) + hoff;
+
+  int kv_valid = N;
+  if (p.seqlens) {
+    const int L = p.seqlens[b];
+    kv_valid = L < 0 ? 0 : (L > N ? N : L);
+  }
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  int kv_end = kv_valid;
+  if (CAUSAL) kv_end = min(kv_end, q0 + BM);
+  const int ntk = (kv_end + BN - 1) / BN;               // tiles the workgroup streams
+  int last = ntk - 1;                                    // last tile this wave needs
+  if (CAUSAL) last = min(last, (qw0 + 31) / BN);
+
+  bf16x8 qf[T::DC];
+  {
+    const int qi = min(qw0 + r32, N - 1);
+    const u32x4* row = reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D);
+#pragma unroll
+    for (int s = 0; s < T::DC; ++s) qf[s] = __builtin_bit_cast(bf16x8, row[2 * s + hi]);
+  }
+  // Per-lane LDS base offsets.  The swizzled chunk index splits into bits that
+  // depend on the lane only and bits that depend on the k-step (K) or the
+  // column block (V), and the two never overlap the row offset, so every
+  // operand address is one XOR of a lane base with a compile-time constant.
+  //   K, k-step s: chunk (2s + hi) ^ kswz(r32) = ((s ^ (x >> 1)) << 1) | (hi ^ (x & 1))
+  //   V, block cb: chunk (4cb + c4) ^ vswz(vrow), vswz a multiple of 2 below 8 (d=64)
+  //                or of 4 below 16 (d=128)
+  const int kx = kswz<D>(r32);
+  const int kbase = r32 * T::ROW + (((kx >> 1) << 1 | (hi ^ (kx & 1))) << 4);   // k-step 0
+  const int i16 = lane & 15;
+  const int g16 = (lane >> 4) & 1;
+  const int vrow = 4 * hi + (i16 >> 2);
+  const int vbase = vrow * T::ROW + (((2 * g16 + ((i16 & 3) >> 1)) ^ vswz<D>(vrow)) << 4) + (i16 & 1) * 8;  // block 0
+  auto koff = [&](int s_) { return kbase ^ (s_ << 5); };
+  auto voff = [&](int cb) { return vbase ^ (cb << 6); };
+  int ld_row[NLD], ld_kc[NLD], ld_vc[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int pos = (wave * NLD + i) * 64 + lane;
+    const int row = pos / T::CH;
+    const int cst = pos % T::CH;
+    ld_row[i] = row;
+    ld_kc[i] = (cst ^ kswz<D>(row)) * 8;
+    ld_vc[i] = (cst ^ vswz<D>(row)) * 8;
+  }
+  auto load_k = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int key = min(t * BN + ld_row[i], N - 1);
+      dma16(Kh + (size_t)key * D + ld_kc[i], kbuf[t & 1] + (wave * NLD + i) * 1024);
+    }
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int key = min(t * BN + ld_row[i], N - 1);
+      dma16(Vh + (size_t)key * D + ld_vc[i], vbuf[t & 1] + (wave * NLD + i) * 1024);
+    }
+  };
+
+  f32x16 oacc[T::DB];
+#pragma unroll
+  for (int cb = 0; cb < T::DB; ++cb) oacc[cb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 sacc[KB];
+  uint32_t pk[KB][8];
+  const float sc = p.scale * kLog2e;
+  bf16x2 ones;
+  ones[0] = (__bf16)1.0f;
+  ones[1] = (__bf16)1.0f;
+
+  // MFMA phase: O^T = alpha O^T + V_{tv}^T P^T (if DO_PV) and S^T = K_{tk} Q^T
+  // (if DO_QK).  Every LDS operand of the phase is requested up front, so the
+  // reads are in flight while the first products run (the scheduling fence
+  // keeps the compiler from pulling them back next to their uses).  The two
+  // products are issued alternately: the DB independent O^T chains cover the
+  // latency of the S^T chain(s).
+  constexpr int NPV = KB * 2 * T::DB;   // MFMAs of O^T += V^T P^T per tile
+  constexpr int NQK = KB * T::DC;       // MFMAs of S^T = K Q^T per tile
+  auto mfma_phase = [&](const bool DO_PV, int tv, const bool DO_QK, int tk) __attribute__((always_inline)) {
+    s16x4 vfr[NPV][2];
+    u32x4 kfr[NQK];
+    if (DO_PV) {
+      const char* Vs = vbuf[tv & 1];
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+        char* vb = const_cast<char*>(Vs) + (kb * 32 + 16 * u) * T::ROW + voff(cb);
+        vfr[i][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+        vfr[i][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * T::ROW));
+      }
+    }
+    if (DO_QK) {
+      const char* Ks = kbuf[tk & 1];
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        const int s = i / KB, kb = i % KB;   // key blocks interleaved: KB chains
+        kfr[i] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * T::ROW + koff(s));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto products = [&]() __attribute__((always_inline)) {
+      if (DO_QK) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+      }
+#pragma unroll
+      for (int i = 0; i < (NPV > NQK ? NPV : NQK); ++i) {
+        if (DO_PV && i < NPV) {
+          const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+          const u32x4 b4 = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, vfr[i][0]);
+          const u32x2 hi2 = __builtin_bit_cast(u32x2, vfr[i][1]);
+          const u32x4 a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), __builtin_bit_cast(bf16x8, b4),
+                                                             oacc[cb], 0, 0, 0);
+        }
+        if (DO_QK && i < NQK) {
+          const int s = i / KB, kb = i % KB;
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr[i]), qf[s], sacc[kb], 0, 0, 0);
+        }
+      }
+    };
+    products();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) pin(sacc[kb]);
+#pragma unroll
+    for (int cb = 0; cb < T::DB; ++cb) pin(oacc[cb]);
+  };
+  // Online softmax of sacc (tile t) into pk.  The mask, where the tile crosses
+  // the valid-key end or this wave's causal diagonal, overwrites sacc in place.
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * BN;
+    const bool need_mask = (k0 + BN > kv_valid) || (CAUSAL && k0 + BN - 1 > qw0);
+    if (need_mask) {
+      const int qi = qw0 + r32;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = key < kv_valid && (!CAUSAL || key <= qi);
+          sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = pair_max(mx);
+    const float tmax = mx * sc;
+    const bool need = tmax > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      keep_branch();
+      const float m_new = need ? tmax : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int cb = 0; cb < T::DB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    }
+    const float mref = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sc, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
+        const uint32_t pp = pack_bf16(p0, p1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run, false);
+        pk[kb][j] = pp;
+      }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pin(pk[kb][j]);
+    pin(l_run);
+  };
+
+  // Global phase counter, identical in every wave.  Phase 2t starts the loads of
+  // K_{t+1} and V_t; phase 2t+1 ends by waiting for them.
+  const int n_phases = 2 * ntk + 2;
+  int ph = 0;
+  auto begin_phase = [&]() __attribute__((always_inline)) {
+    if ((ph & 1) == 0) {
+      const int t = ph >> 1;
+      if (t < ntk) {
+        if (t + 1 < ntk) load_k(t + 1);
+        load_v(t);
+      }
+    }
+  };
+  auto end_phase = [&]() __attribute__((always_inline)) {
+    if (ph & 1) wait_vmem();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    ++ph;
+  };
+  if (ntk > 0) {
+    load_k(0);
+    wait_vmem();
+    __syncthreads();
+    if (grp == 1) {              // the second group starts one phase late
+      begin_phase();
+      end_phase();
+    }
+    if (last >= 0) {
+      begin_phase();
+      mfma_phase(false, 0, true, 0);
+      end_phase();
+      for (int t = 0; t < last; ++t) {
+        begin_phase();
+        softmax(t);
+        end_phase();
+        begin_phase();
+        mfma_phase(true, t, true, t + 1);
+        end_phase();
+      }
+      begin_phase();
+      softmax(last);
+      end_phase();
+      begin_phase();
+      mfma_phase(true, last, false, 0);
+      end_phase();
+    }
+    while (ph < n_phases) {      // keep loading and meeting the barriers
+      begin_phase();
+      end_phase();
+    }
+  }
+
+  const float l = pair_sum(l_run);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  const int qi = qw0 + r32;
+  if (qi < N) {
+    __bf16* orow = Oh + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < T::DB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = cb * 32 + 8 * g + 4 * hi;
+        const u32x2 w = {pack_bf16(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv),
+                         pack_bf16(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + col) = w;
+      }
+    if (p.lse && hi == 0) p.lse[(size_t)bh * N + qi] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int BN, bool CAUSAL>
+hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
+  const int ntiles = (p.N + 255) / 256;
+  const dim3 grid((unsigned)ntiles * (unsigned)p.H * (unsigned)p.B);
+  FwdParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_pp_kernel<D, BN, CAUSAL>), grid, dim3(512), args, 0, stream);
+}
+
+template <int D, int QB, int BN, int OCC, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr int BM = kWaves * 32 * QB;
   const int ntiles = (p.N + BM - 1) / BM;
   const dim3 grid((unsigned)ntiles * (unsigned)p.H * (unsigned)p.B);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, QB, CAUSAL>), grid, dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, QB, BN, OCC, CAUSAL>), grid, dim3(kThreads), args, 0,
+                         stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, 2, true>(p, stream) : launch<64, 2, false>(p, stream);
-  return p.causal ? launch<128, 2, true>(p, stream) : launch<128, 2, false>(p, stream);
+  // The ping-pong kernel (8 waves, 256 query rows per workgroup) needs at least
+  // one workgroup per compute unit (256 on MI355X), and for causal problems,
+  // whose workgroups differ in length, several; smaller problems use the 4-wave
+  // kernel with 128 rows per workgroup and two workgroups per compute unit.
+  const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
+  const bool pp = pp_groups >= (p.causal ? 1024 : 256);
+  if (p.d == 64) {
+    if (pp) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
+    return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
+  }
+  if (pp) return p.causal ? launch_pp<128, 32, true>(p, stream) : launch_pp<128, 32, false>(p, stream);
+  return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }
 
 }  // namespace fa

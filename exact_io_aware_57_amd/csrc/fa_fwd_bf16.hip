@@ -553,24 +553,26 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   constexpr int NPV = KB * 2 * T::DB;   // MFMAs of O^T += V^T P^T per tile
   constexpr int NQK = KB * T::DC;       // MFMAs of S^T = K Q^T per tile
   auto mfma_phase = [&](const bool DO_PV, int tv, const bool DO_QK, int tk) __attribute__((always_inline)) {
+    // K operands are requested up front (they feed the longer S^T chain); the V
+    // operands are read next to their products when the tile has more than one
+    // key block, so the registers for all of them are not needed at once.
+    constexpr bool V_UPFRONT = (KB == 1);
     s16x4 vfr[NPV][2];
     u32x4 kfr[NQK];
-    if (DO_PV) {
-      const char* Vs = vbuf[tv & 1];
+    const char* Vs = vbuf[tv & 1];
+    const char* Ks = kbuf[tk & 1];
+    auto read_v = [&](int i) __attribute__((always_inline)) {
+      const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+      char* vb = const_cast<char*>(Vs) + (kb * 32 + 16 * u) * T::ROW + voff(cb);
+      vfr[i][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+      vfr[i][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * T::ROW));
+    };
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
-        char* vb = const_cast<char*>(Vs) + (kb * 32 + 16 * u) * T::ROW + voff(cb);
-        vfr[i][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
-        vfr[i][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * T::ROW));
-      }
-    }
-    if (DO_QK) {
-      const char* Ks = kbuf[tk & 1];
-#pragma unroll
-      for (int i = 0; i < NQK; ++i) {
-        const int s = i / KB, kb = i % KB;   // key blocks interleaved: KB chains
-        kfr[i] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * T::ROW + koff(s));
+    for (int i = 0; i < (NPV > NQK ? NPV : NQK); ++i) {
+      if (V_UPFRONT && DO_PV && i < NPV) read_v(i);
+      if (DO_QK && i < NQK) {
+        const int s_ = i / KB, kb = i % KB;   // key blocks interleaved: KB chains
+        kfr[i] = *reinterpret_cast<const u32x4*>(Ks + kb * 32 * T::ROW + koff(s_));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -581,6 +583,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int i = 0; i < (NPV > NQK ? NPV : NQK); ++i) {
+        if (!V_UPFRONT && DO_PV && i < NPV) read_v(i);
         if (DO_PV && i < NPV) {
           const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
           const u32x4 b4 = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
@@ -759,7 +762,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     if (pp) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }
-  if (pp) return p.causal ? launch_pp<128, 32, true>(p, stream) : launch_pp<128, 32, false>(p, stream);
+  if (pp) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
   return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }
 

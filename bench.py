@@ -200,18 +200,65 @@ def cpu_baseline(index, heads):
                       f"full score matrix), {dt:.2f} s, {flops / 1e9:.1f} GFLOP algorithmic; host cores visible: {cores}"}
 
 
+def summarize_traffic(fetch_csv, write_csv, workload_name, command):
+    """Write profiles/traffic_<workload>.txt from two rocprofv3 --pmc CSV files.
+
+    The attention kernel's counter values are averaged over its dispatches; the
+    calibration copy is the __amd_rocclr_copyBuffer dispatch with the largest
+    reading (the --calib-copy-mb copy: that many MiB read and written).
+    """
+    import csv
+
+    def load(path, counter):
+        fa, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "fwd_bf16" in r["Kernel_Name"]:
+                fa.append(v)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+        return sum(fa) / len(fa), max(copy), len(fa)
+
+    f_fa, f_copy, n_f = load(fetch_csv, "FETCH_SIZE")
+    w_fa, w_copy, n_w = load(write_csv, "WRITE_SIZE")
+    mb = None
+    for tok in command.split("--calib-copy-mb")[1:]:
+        mb = int(tok.split()[0])
+    copy_bytes = mb * (1 << 20)
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.txt")
+    with open(path, "w") as out:
+        out.write(f"# HBM traffic of the fused attention kernel, workload {workload_name}\n")
+        out.write("# two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE), values in KiB per dispatch;\n")
+        out.write(f"# the same counters on a device copy of {mb} MiB calibrate KiB -> bytes.\n")
+        out.write(f"# command (each pass): {command}\n")
+        out.write(f"kernel_source_sha = {kernel_source_hash()}\n")
+        out.write(f"dispatches_fetch = {n_f}\ndispatches_write = {n_w}\n")
+        out.write(f"fetch_kib_per_dispatch = {f_fa:.1f}\nwrite_kib_per_dispatch = {w_fa:.1f}\n")
+        out.write(f"copy_bytes = {copy_bytes}\ncopy_fetch_kib = {f_copy:.1f}\ncopy_write_kib = {w_copy:.1f}\n")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=5, help="workload index (1..5); default: long-context causal d=128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="whole heads the CPU oracle times")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other bf16 workloads")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (a known-size kernel for counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write profiles/traffic_<workload>.txt from two rocprofv3 --pmc CSV files and exit")
     args = ap.parse_args(argv)
+
+    if args.summarize_traffic:
+        from exact_io_aware_57_amd.inputs import workload
+        print(summarize_traffic(*args.summarize_traffic[:2], workload(args.workload).name, args.summarize_traffic[2]))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "

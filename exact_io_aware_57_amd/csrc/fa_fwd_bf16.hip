@@ -545,11 +545,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   ones[1] = (__bf16)1.0f;
 
   // MFMA phase: O^T = alpha O^T + V_{tv}^T P^T (if DO_PV) and S^T = K_{tk} Q^T
-  // (if DO_QK).  Every LDS operand of the phase is requested up front, so the
-  // reads are in flight while the first products run (the scheduling fence
-  // keeps the compiler from pulling them back next to their uses).  The two
-  // products are issued alternately: the DB independent O^T chains cover the
-  // latency of the S^T chain(s).
+  // (if DO_QK).  The K operands are requested up front (the scheduling fence
+  // keeps the compiler from pulling them back next to their uses).  With both
+  // products, S^T runs first and the V operand reads are interleaved with it;
+  // a phase with one product only issues its products in order.
   constexpr int NPV = KB * 2 * T::DB;   // MFMAs of O^T += V^T P^T per tile
   constexpr int NQK = KB * T::DC;       // MFMAs of S^T = K Q^T per tile
   auto mfma_phase = [&](const bool DO_PV, int tv, const bool DO_QK, int tk) __attribute__((always_inline)) {
@@ -599,7 +598,44 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
         }
       }
     };
-    products();
+    if (!(DO_PV && DO_QK)) {
+      products();
+    } else {
+      // Both products: S^T first, since its operands (K) were requested
+      // first; the V operands are requested two reads per S^T product, so
+      // they arrive while the matrix core works through S^T, and O^T += V^T
+      // P^T runs last without waiting on LDS.
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        const int s = i / KB, kb = i % KB;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kfr[i]), qf[s], sacc[kb], 0, 0, 0);
+      }
+      if (!V_UPFRONT) {
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) read_v(i);
+      }
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+        const u32x4 b4 = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, vfr[i][0]);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, vfr[i][1]);
+        const u32x4 a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), __builtin_bit_cast(bf16x8, b4),
+                                                           oacc[cb], 0, 0, 0);
+      }
+      if (!V_UPFRONT) {
+        constexpr int RPM = (2 * NPV + NQK - 1) / NQK;   // V reads per S^T product
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);   // then RPM LDS reads
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NPV, 0);
+      }
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) pin(sacc[kb]);
 #pragma unroll

@@ -30,11 +30,14 @@
 //    gfx950 transposing LDS read ds_read_b64_tr_b16.  Each lane again holds one
 //    query's outputs, so the softmax rescale is a per-lane scalar.
 //  * Non-matmul work per score: one FMA (scale and max subtraction folded), one
-//    v_exp_f32 (base 2), a third of a v_max3, half a v_cvt_pk_bf16_f32 and half
-//    a v_dot2 (the row sum over the same bf16-rounded P that feeds the second
-//    product).  The output is rescaled only when a row max grows by more than
-//    2^8 in the exponent (the result is the same; P may reach 2^8 in between),
-//    and divided by the row sum once at the end.
+//    v_exp_f32 (base 2), half a v_cvt_pk_bf16_f32 and half a v_dot2 (the row
+//    sum over the same bf16-rounded P that feeds the second product).  The
+//    reference max of a row changes rarely: the 4-wave kernel moves it when a
+//    tile's max exceeds it by more than 2^8 in the exponent; the 8-wave kernel
+//    does not even compute a tile's max unless the tile's sum of P exceeds
+//    2^8, which every P <= 2^8 rules out (the result is the same either way;
+//    P may reach 2^8 in between).  The output is divided by the row sum once
+//    at the end.
 //  * Masks are applied only on tiles that straddle a boundary (causal diagonal,
 //    last valid key), in a separate instantiation of the tile body; tiles wholly
 //    above a wave's causal diagonal are skipped.
@@ -63,6 +66,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+constexpr float kMaxTileSum = 256.0f;   // 2^kTau
 
 template <int D, int BN>
 struct Tile {
@@ -657,36 +661,46 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
           sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // Exponentials against the current reference max, without computing
+    // this tile's max: every p is at most 2^kTau whenever the lane's sum of
+    // its p over the tile is (all p are >= 0), so the max is computed only
+    // on the rare tiles where that sum is larger (or not a number, or the
+    // row has no reference yet); those tiles are recomputed against it.
+    auto exps = [&](float mref) __attribute__((always_inline)) {
+      float ls = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = pair_max(mx);
-    const float tmax = mx * sc;
-    const bool need = tmax > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sc, -mref));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
+          const uint32_t pp = pack_bf16(p0, p1);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, ls, false);
+          pk[kb][j] = pp;
+        }
+      return ls;
+    };
+    float ls = exps(m_run == -INFINITY ? 0.0f : m_run);
+    const bool bad = !(ls <= kMaxTileSum) || m_run == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       keep_branch();
-      const float m_new = need ? tmax : m_run;
-      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx * sc);
+      const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int cb = 0; cb < T::DB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      ls = exps(m_run == -INFINITY ? 0.0f : m_run);
     }
-    const float mref = (m_run == -INFINITY) ? 0.0f : m_run;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sc, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
-        const uint32_t pp = pack_bf16(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run, false);
-        pk[kb][j] = pp;
-      }
+    l_run += ls;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

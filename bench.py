@@ -164,6 +164,33 @@ def time_launches(launch, steps, warmup):
     return (t1 - t0) * 1e3 / steps, sum(per_launch) / len(per_launch), min(per_launch)
 
 
+def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=True, std=0.5, seed=6, steps=20):
+    """Kernel time of fa_fwd_gqa on seeded inputs of the given shape."""
+    import torch
+
+    from exact_io_aware_57_amd import binding
+    from exact_io_aware_57_amd.inputs import random_qkv_grouped
+
+    q, k, v, _ = random_qkv_grouped(B, H, H_kv, N, d, torch.bfloat16, std, seed)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+    def launch():
+        st = binding.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, N, d,
+                                scale, causal, None, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd_gqa failed: {binding.fa_status_str(st)}")
+
+    m_step, m_kern, _ = time_launches(launch, steps, 10)
+    flops = algorithmic_flops(B, H, N, d, causal)
+    return {"workload": f"long_context_gqa: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 {'causal' if causal else 'non-causal'}",
+            "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
+            "tflops": round(flops / (m_kern * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(index, heads):
     """The oracle as it stands on `heads` whole heads of the workload."""
     import numpy as np
@@ -306,6 +333,9 @@ def main(argv=None):
                 entry["frac_of_hbm_peak"] = round(p.bytes / (m_kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
             others[w.name] = entry
             del p
+        # grouped-query variant of the long-context shape (8 key/value heads
+        # shared by groups of 4 query heads): same FLOP, a quarter of the K/V
+        others["long_context_gqa"] = time_grouped(dev, stream.cuda_stream)
 
     traffic = read_traffic(wl.name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the attention forward pass runs in the
 HIP kernels of libfa_mi355x.so.  ``fa_fwd``, ``fa_fwd_f32`` and
-``fa_status_str`` mirror the C entry points one to one (raw device pointers as
+``fa_fwd_gqa``, ``fa_fwd_gqa_f32`` and ``fa_status_str`` mirror the C entry points one to one (raw device pointers as
 ints, a hipStream_t as an int or None).  ``attention_forward`` is a convenience
 wrapper for torch device tensors: it checks shapes, dtypes and layout, takes
 the pointers and the current stream, and raises ``FaError`` on a non-zero
@@ -21,7 +21,7 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_NO_DEVICE = -4
 FA_ERR_LAUNCH = -5
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -53,6 +53,10 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
             fn.restype = i32
+        for name in ("fa_fwd_gqa", "fa_fwd_gqa_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+            fn.restype = i32
         lib.fa_status_str.argtypes = [i32]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -75,22 +79,38 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, stream):
                              float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, seqlens, stream):
+    """C fa_fwd_gqa with integer device pointers (k, v have H_kv heads)."""
+    return load().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
+                             float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, seqlens, stream):
+    """C fa_fwd_gqa_f32 with integer device pointers (k, v have H_kv heads)."""
+    return load().fa_fwd_gqa_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
+                                 float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
 def fa_status_str(status):
     return load().fa_status_str(int(status)).decode()
 
 
 def attention_forward(q, k, v, scale, causal=False, seqlens=None, out=None, lse=None, stream=None, want_lse=True):
-    """O (and LSE) for torch device tensors q, k, v of shape [B, H, N, d].
+    """O (and LSE) for torch device tensors q [B, H, N, d] and k, v [B, H_kv, N, d].
 
-    bf16 tensors go to fa_fwd, float32 tensors to fa_fwd_f32.  ``out``/``lse``
+    H_kv = H goes to fa_fwd / fa_fwd_f32 (bf16 / float32 tensors), a smaller
+    H_kv (dividing H: grouped or multi-query attention) to fa_fwd_gqa /
+    fa_fwd_gqa_f32.  ``out``/``lse``
     may be given (they must have the right shape, dtype and be contiguous);
     otherwise they are allocated with torch.  ``stream`` defaults to torch's
     current stream.  Returns (out, lse or None).
     """
     import torch
 
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if (q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]
+            or k.shape[1] < 1 or q.shape[1] % k.shape[1]):
+        raise ValueError(f"need q [B, H, N, d] and k, v [B, H_kv, N, d] with H_kv dividing H, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -111,10 +131,15 @@ def attention_forward(q, k, v, scale, causal=False, seqlens=None, out=None, lse=
         raise ValueError("seqlens must be an int32 [B] device tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            None if lse is None else lse.data_ptr(), B, H, N, d, scale, causal,
-            None if seqlens is None else seqlens.data_ptr(), stream)
+    H_kv = k.shape[1]
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr())
+    tail = (N, d, scale, causal, None if seqlens is None else seqlens.data_ptr(), stream)
+    if H_kv == H:
+        fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+        st = fn(*args, B, H, *tail)
+    else:
+        fn = fa_fwd_gqa if q.dtype == torch.bfloat16 else fa_fwd_gqa_f32
+        st = fn(*args, B, H, H_kv, *tail)
     if st != FA_OK:
         raise FaError(st, fn.__name__)
     return out, lse

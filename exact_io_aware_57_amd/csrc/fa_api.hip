@@ -42,6 +42,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int validate(const fa::FwdParams& p) {
   if (!p.q || !p.k || !p.v || !p.o) return FA_ERR_INVALID_ARG;
   if (p.B < 1 || p.H < 1 || p.N < 1) return FA_ERR_INVALID_ARG;
+  if (p.Hkv < 1 || p.Hkv > p.H || p.H % p.Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(p.scale) || !(p.scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (p.d != 64 && p.d != 128) return FA_ERR_UNSUPPORTED;
   // Every element offset must fit the 64-bit index arithmetic of the kernels and
@@ -72,21 +73,36 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,
            const int32_t* seqlens, void* stream) {
-  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, scale, causal ? 1 : 0};
+  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, H, scale, causal ? 1 : 0};
   return run(p, stream, true);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const int32_t* seqlens, void* stream) {
-  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, scale, causal ? 1 : 0};
+  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, H, scale, causal ? 1 : 0};
+  return run(p, stream, false);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal,
+               const int32_t* seqlens, void* stream) {
+  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, H_kv, scale, causal ? 1 : 0};
+  return run(p, stream, true);
+}
+
+int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal,
+                   const int32_t* seqlens, void* stream) {
+  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, H_kv, scale, causal ? 1 : 0};
   return run(p, stream, false);
 }
 
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
-    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: null tensor, non-positive size, bad scale or size overflow";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: null tensor, non-positive size, key/value heads not dividing heads, bad scale or size overflow";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension not 64/128, or device is not gfx950";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte alignment, lse/seqlens 4-byte";
     case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no current HIP device";

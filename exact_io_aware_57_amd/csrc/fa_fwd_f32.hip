@@ -40,9 +40,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p) {
   const int qt = blockIdx.x - bh * ntiles;
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
+  // key/value head of this query head: groups of H / Hkv consecutive heads
+  const size_t kvoff = ((size_t)b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * (size_t)N * D;
   const float* __restrict__ Qh = reinterpret_cast<const float*>(p.q) + hoff;
-  const float* __restrict__ Kh = reinterpret_cast<const float*>(p.k) + hoff;
-  const float* __restrict__ Vh = reinterpret_cast<const float*>(p.v) + hoff;
+  const float* __restrict__ Kh = reinterpret_cast<const float*>(p.k) + kvoff;
+  const float* __restrict__ Vh = reinterpret_cast<const float*>(p.v) + kvoff;
   float* __restrict__ Oh = reinterpret_cast<float*>(p.o) + hoff;
 
   int kv_valid = N;

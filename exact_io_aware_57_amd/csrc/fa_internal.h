@@ -16,6 +16,7 @@ struct FwdParams {
   float* lse;               // may be null
   const int32_t* seqlens;   // may be null
   int B, H, N, d;
+  int Hkv;                  // key/value heads; divides H (H: plain multi-head)
   float scale;
   int causal;
 };

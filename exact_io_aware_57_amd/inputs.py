@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "random_qkv", "random_seqlens"]
+__all__ = ["Workload", "WORKLOADS", "workload", "make_inputs", "random_qkv", "random_qkv_grouped", "random_seqlens"]
 
 
 @dataclass(frozen=True)
@@ -85,6 +85,22 @@ def random_qkv(B, H, N, d, dtype=torch.bfloat16, std=1.0, seed=0, len_range=None
     shape = (B, H, N, d)
     out = []
     for _ in range(3):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        out.append(x.to(dtype).contiguous())
+    seqlens = None
+    if len_range is not None:
+        seqlens = random_seqlens(B, len_range[0], len_range[1], g)
+    return out[0], out[1], out[2], seqlens
+
+
+def random_qkv_grouped(B, H, H_kv, N, d, dtype=torch.bfloat16, std=1.0, seed=0, len_range=None):
+    """Q as [B, H, N, d] and K, V as [B, H_kv, N, d] CPU tensors (+ seqlens or None),
+    drawn like ``random_qkv`` (q, k, v, then the lengths, from one seeded generator)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for shape in ((B, H, N, d), (B, H_kv, N, d), (B, H_kv, N, d)):
         x = torch.randn(shape, generator=g, dtype=torch.float32)
         if std != 1.0:
             x = x * std

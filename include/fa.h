@@ -52,7 +52,7 @@ extern "C" {
 
 typedef enum fa_status {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* NULL tensor, B/H/N < 1, non-finite or non-positive scale, size overflow */
+  FA_ERR_INVALID_ARG = -1, /* NULL tensor, B/H/N < 1, H_kv not dividing H, bad scale, size overflow */
   FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, or the current device is not gfx950 */
   FA_ERR_MISALIGNED = -3,  /* q, k, v, o not 16-byte aligned, or lse / seqlens not 4-byte aligned */
   FA_ERR_NO_DEVICE = -4,   /* no HIP device is present or current */
@@ -86,6 +86,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                const int32_t* seqlens, void* stream);
+
+/*
+ * Grouped-query / multi-query forward pass (FlashAttention (UR), section
+ * "FlashAttention-2 (2023)": multi-query attention among the supported
+ * architectures).  q and o are [B, H, N, d]; k and v are [B, H_kv, N, d] with
+ * 1 <= H_kv <= H and H_kv dividing H.  Query heads
+ * g*(H/H_kv) .. (g+1)*(H/H_kv)-1 attend to key/value head g: H_kv = H is
+ * fa_fwd, H_kv = 1 is multi-query attention.  Every other argument, the
+ * arithmetic and the errors are those of fa_fwd (bf16) and fa_fwd_f32 (float);
+ * an H_kv that does not divide H returns FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal,
+               const int32_t* seqlens, void* stream);
+int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal,
+                   const int32_t* seqlens, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -17,10 +17,11 @@ oracle.  Everything is float64.
 Modules
 -------
 attention : the definition in numpy float64 (``attention``, ``attention_rows``,
-            ``softmax_matrix``).  Every function is pinned by tests/test_oracle.py.
+            ``softmax_matrix``, ``kv_head`` for grouped / multi-query
+            attention).  Every function is pinned by tests/test_oracle.py.
 brute     : the same definition as scalar Python loops with ``math.exp`` and
             ``math.fsum`` and no max shift; a second, independent code path used
             only to pin ``attention`` on tiny inputs.
 """
-from .attention import attention, attention_rows, softmax_matrix, allowed_mask  # noqa: F401
+from .attention import attention, attention_rows, softmax_matrix, allowed_mask, kv_head  # noqa: F401
 from .brute import attention_brute  # noqa: F401

@@ -26,7 +26,7 @@ LSE_i = log(sum_{j allowed} exp(s_ij)), computed stably as m_i + log(l_i).
 """
 import numpy as np
 
-__all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention"]
+__all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention", "kv_head"]
 
 
 def _f64(x):
@@ -71,17 +71,35 @@ def softmax_matrix(q_rows, k_head, scale, rows, valid_len, causal):
     return p, m, l
 
 
+def kv_head(h, n_heads, n_kv_heads):
+    """Key/value head read by query head h.
+
+    FlashAttention (UR), section "FlashAttention-2 (2023)", names multi-query
+    attention (all query heads share one key/value head) among the supported
+    architectures.  The reading used here is the grouped form that contains it:
+    with H_kv key/value heads, H_kv dividing H, query heads
+    g*(H/H_kv) .. (g+1)*(H/H_kv)-1 share key/value head g.  H_kv = H is ordinary
+    multi-head attention and H_kv = 1 is multi-query attention.
+    """
+    if n_kv_heads < 1 or n_heads % n_kv_heads:
+        raise ValueError("the number of key/value heads must divide the number of query heads")
+    return h // (n_heads // n_kv_heads)
+
+
 def attention_rows(q, k, v, scale, causal, seqlens, b, h, rows):
     """O and LSE of the listed query rows of head (b, h) only.
 
-    q, k, v are [B, H, N, d]; returns O [len(rows), d] and LSE [len(rows)] in
-    float64.  Used where the whole output is too large to check one by one.
+    q is [B, H, N, d]; k, v are [B, H_kv, N, d] (H_kv = H, or a divisor of H for
+    grouped / multi-query attention, see ``kv_head``).  Returns O [len(rows), d]
+    and LSE [len(rows)] in float64.  Used where the whole output is too large to
+    check one by one.
     """
     rows = np.asarray(rows, dtype=np.int64)
     n_keys = k.shape[2]
     valid = _valid_len(seqlens, b, n_keys)
-    p, m, l = softmax_matrix(_f64(q[b, h][rows]), k[b, h], scale, rows, valid, causal)
-    o = p @ _f64(v[b, h])
+    g = kv_head(h, q.shape[1], k.shape[1])
+    p, m, l = softmax_matrix(_f64(q[b, h][rows]), k[b, g], scale, rows, valid, causal)
+    o = p @ _f64(v[b, g])
     nonempty = l > 0
     lse = np.full(rows.size, -np.inf)
     lse[nonempty] = m[nonempty] + np.log(l[nonempty])
@@ -91,6 +109,9 @@ def attention_rows(q, k, v, scale, causal, seqlens, b, h, rows):
 def attention(q, k, v, scale, causal=False, seqlens=None, row_block=2048):
     """Full forward pass: O [B, H, N, d] and LSE [B, H, N], float64.
 
+    k and v may have fewer heads than q (grouped / multi-query attention, see
+    ``kv_head``).
+
     The score matrix is built per head, ``row_block`` query rows at a time, which
     only bounds the memory: the softmax of a row never looks at another row.
     """
@@ -98,8 +119,9 @@ def attention(q, k, v, scale, causal=False, seqlens=None, row_block=2048):
     k = _f64(k)
     v = _f64(v)
     B, H, N, d = q.shape
-    if k.shape != (B, H, k.shape[2], d) or v.shape[:3] != k.shape[:3]:
+    if k.shape[0] != B or k.shape[3] != d or v.shape[:3] != k.shape[:3]:
         raise ValueError("q, k, v shapes disagree")
+    kv_head(0, H, k.shape[1])   # checks that H_kv divides H
     o = np.zeros((B, H, N, v.shape[3]))
     lse = np.full((B, H, N), -np.inf)
     for b in range(B):

@@ -30,7 +30,7 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_status_str"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -97,6 +97,8 @@ def _no_gpu_visible():
 def test_no_device_is_reported(lib):
     assert call(binding.fa_fwd) == binding.FA_ERR_NO_DEVICE
     assert call(binding.fa_fwd_f32) == binding.FA_ERR_NO_DEVICE
+    assert call_gqa(binding.fa_fwd_gqa) == binding.FA_ERR_NO_DEVICE
+    assert call_gqa(binding.fa_fwd_gqa_f32) == binding.FA_ERR_NO_DEVICE
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -109,3 +111,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_ctypes_signatures(lib):
     assert lib.fa_fwd.restype is ctypes.c_int
     assert len(lib.fa_fwd.argtypes) == 13 and len(lib.fa_fwd_f32.argtypes) == 13
+    assert len(lib.fa_fwd_gqa.argtypes) == 14 and len(lib.fa_fwd_gqa_f32.argtypes) == 14
+
+
+GQA_ARGS = dict(ARGS, H=4, H_kv=2)
+
+
+def call_gqa(fn, **over):
+    a = dict(GQA_ARGS)
+    a.update(over)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["scale"], a["causal"],
+              a["seqlens"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", [binding.fa_fwd_gqa, binding.fa_fwd_gqa_f32], ids=["bf16", "f32"])
+def test_grouped_head_counts_are_checked_on_the_host(lib, fn):
+    E = binding
+    for H, H_kv in ((4, 0), (4, -1), (4, 3), (4, 8), (6, 4)):
+        assert call_gqa(fn, H=H, H_kv=H_kv) == E.FA_ERR_INVALID_ARG, (H, H_kv)
+    assert call_gqa(fn, q=None) == E.FA_ERR_INVALID_ARG
+    assert call_gqa(fn, d=96) == E.FA_ERR_UNSUPPORTED
+    assert call_gqa(fn, k=FAKE + 4) == E.FA_ERR_MISALIGNED

@@ -222,3 +222,69 @@ def test_pins_catch_planted_mistake(bug):
 
 def test_oracle_exports():
     assert oracle.attention is attention and callable(oracle.attention_brute)
+
+
+# ---------------------------------------------------------------------------------
+# Grouped / multi-query attention (FlashAttention (UR), section "FlashAttention-2
+# (2023)": multi-query attention among the supported architectures).
+# ---------------------------------------------------------------------------------
+def _brute_grouped(q, k, v, scale, causal, seqlens):
+    """Expected output written out head by head: query head h of a group of
+    H / H_kv consecutive heads reads key/value head h // (H / H_kv); each head is
+    then plain attention, computed by the scalar brute force."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    group = H // Hkv
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.zeros(q.shape[:3])
+    for h in range(H):
+        g = h // group
+        ob, lb = oracle.attention_brute(q[:, h:h + 1].tolist(), k[:, g:g + 1].tolist(), v[:, g:g + 1].tolist(), scale, causal,
+                                        seqlens)
+        o[:, h] = np.array(ob)[:, 0]
+        lse[:, h] = np.array(lb)[:, 0]
+    return o, lse
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (6, 2), (4, 1), (3, 1)])
+@pytest.mark.parametrize("causal,padded", [(False, False), (True, False), (False, True), (True, True)])
+def test_grouped_heads_match_brute_force(H, Hkv, causal, padded):
+    rng = np.random.default_rng(100 + 10 * H + Hkv)
+    B, N, d = 2, 7, 5
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, Hkv, N, d))
+    v = rng.normal(size=(B, Hkv, N, 3))
+    seqlens = rng.integers(0, N + 1, size=B) if padded else None
+    o, lse = attention(q, k, v, 0.7, causal, seqlens)
+    o_ref, lse_ref = _brute_grouped(q, k, v, 0.7, causal, seqlens)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_multi_query_heads_share_keys_and_values():
+    # H_kv = 1: two query heads with equal queries give equal outputs; different
+    # queries over the same keys/values give outputs in the convex hull of V.
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(1, 3, 6, 4))
+    q[0, 2] = q[0, 0]
+    k = rng.normal(size=(1, 1, 6, 4))
+    v = rng.normal(size=(1, 1, 6, 2))
+    o, _ = attention(q, k, v, 0.5, False)
+    np.testing.assert_array_equal(o[0, 0], o[0, 2])
+    assert np.all(o[0] <= v[0, 0].max(axis=0) + 1e-12) and np.all(o[0] >= v[0, 0].min(axis=0) - 1e-12)
+
+
+def test_grouped_pin_catches_a_wrong_head_map(monkeypatch):
+    # Planted on the CPU: interleaved instead of consecutive groups.
+    import importlib
+    oa = importlib.import_module("oracle.attention")   # the module (the package re-exports a function of that name)
+    monkeypatch.setattr(oa, "kv_head", lambda h, n, nkv: h % nkv)
+    with pytest.raises(AssertionError):
+        test_grouped_heads_match_brute_force(4, 2, False, False)
+
+
+def test_head_counts_must_divide():
+    q = np.zeros((1, 4, 3, 2))
+    k = np.zeros((1, 3, 3, 2))
+    with pytest.raises(ValueError):
+        attention(q, k, k, 1.0)

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from exact_io_aware_57_amd import binding
-from exact_io_aware_57_amd.inputs import make_inputs, random_qkv, workload
+from exact_io_aware_57_amd.inputs import make_inputs, random_qkv, random_qkv_grouped, workload
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -111,6 +111,76 @@ def test_workload5_sampled_rows():
     # every row is a convex combination of value rows: within the column range of V
     vmax = v.float().abs().amax(dim=(2, 3)).cpu()
     assert (og.abs().amax(dim=(2, 3)) <= vmax * (1 + 2 ** -7)).all()
+
+
+def check_sampled_rows(q, k, v, scale, causal, seqlens, heads, tag, n_rows=40, seed=0):
+    """Full-size call; sampled rows of the listed (b, h) heads against the oracle."""
+    say(f"[parity] {tag}: q {tuple(q.shape)} k {tuple(k.shape)} causal={causal} padded={seqlens is not None}")
+    o, lse = gpu_forward(q, k, v, scale, causal, seqlens)
+    og, lg = np64(o), np64(lse)
+    assert np.isfinite(og).all()
+    N = q.shape[2]
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 255, 256, N - 2, N - 1], rng.integers(0, N, size=n_rows)]))
+    rows = rows[(rows >= 0) & (rows < N)]
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    sl = None if seqlens is None else seqlens.numpy()
+    worst, worst_l, total, count = 0.0, 0.0, 0.0, 0
+    for b, h in heads:
+        o_ref, lse_ref = oracle.attention_rows(qn, kn, vn, scale, causal, sl, b, h, rows)
+        e = np.abs(og[b, h, rows] - o_ref)
+        worst, total, count = max(worst, e.max()), total + e.sum(), count + e.size
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lg[b, h, rows]), fin)
+        if fin.any():
+            worst_l = max(worst_l, np.abs(lg[b, h, rows][fin] - lse_ref[fin]).max())
+    say(f"[parity] {tag}: O max {worst:.3e} mean {total / count:.3e} LSE max {worst_l:.3e}")
+    assert worst <= BF16_MAX and total / count <= BF16_MEAN and worst_l <= BF16_LSE
+
+
+# Grids large enough for the 8-wave kernel (at least 256 workgroups of 256 rows,
+# 1024 when causal); the small shapes elsewhere in this file run the 4-wave one.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_kernel(d, causal):
+    B, H, N = 2, 16, (8192 if causal else 2048)
+    q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=31 + d + causal)
+    check_sampled_rows(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (1, 9), (1, 15)], f"large grid d={d}",
+                       seed=d + causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(8, 4), (8, 2), (6, 1)])
+def test_grouped_query_parity(H, H_kv, d, causal):
+    for n, lens in [(200, None), (333, (1, 333))]:
+        q, k, v, seqlens = random_qkv_grouped(2, H, H_kv, n, d, torch.bfloat16, 1.0, seed=40 + H_kv + n, len_range=lens)
+        check_against_oracle(q, k, v, 1.0 / math.sqrt(d), causal, seqlens, fp32=False,
+                             tag=f"grouped H={H} H_kv={H_kv} n={n} d={d}")
+
+
+def test_grouped_query_fp32():
+    q, k, v, seqlens = random_qkv_grouped(2, 4, 2, 150, 64, torch.float32, 1.0, seed=5, len_range=(20, 150))
+    check_against_oracle(q, k, v, 0.125, True, seqlens, fp32=True, tag="grouped fp32")
+
+
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, False)])
+def test_grouped_query_large_grid(d, causal):
+    # multi-query (H_kv = 1) and groups of 4 on the 8-wave kernel
+    for H_kv in (1, 8):
+        N = 8192 if causal else 2048
+        q, k, v, _ = random_qkv_grouped(1, 32, H_kv, N, d, torch.bfloat16, 1.0, seed=70 + H_kv)
+        check_sampled_rows(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (0, 5), (0, 31)],
+                           f"grouped large H_kv={H_kv} d={d}", seed=H_kv)
+
+
+def test_grouped_query_equals_repeated_heads():
+    # the kernel's grouped path against its own plain path on repeated K/V: bitwise equal
+    q, k, v, _ = random_qkv_grouped(2, 8, 2, 257, 128, torch.bfloat16, 1.0, seed=9)
+    o1, l1 = gpu_forward(q, k, v, 0.0884, True, None)
+    kr, vr = k.repeat_interleave(4, dim=1).contiguous(), v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = gpu_forward(q, kr, vr, 0.0884, True, None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 RAGGED_N = [1, 2, 3, 7, 8, 31, 33, 63, 64, 65, 100, 127, 129, 255, 256, 257, 300, 513, 1000]

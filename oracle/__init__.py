@@ -18,10 +18,14 @@ Modules
 -------
 attention : the definition in numpy float64 (``attention``, ``attention_rows``,
             ``softmax_matrix``, ``kv_head`` for grouped / multi-query
-            attention).  Every function is pinned by tests/test_oracle.py.
+            attention, ``attention_decode`` for a few queries against a key
+            cache, ``merge_partials`` for combining results over disjoint key
+            sets).  Every function is pinned by tests/test_oracle.py.
 brute     : the same definition as scalar Python loops with ``math.exp`` and
             ``math.fsum`` and no max shift; a second, independent code path used
             only to pin ``attention`` on tiny inputs.
 """
-from .attention import attention, attention_rows, softmax_matrix, allowed_mask, kv_head  # noqa: F401
+from .attention import (  # noqa: F401
+    allowed_mask, attention, attention_decode, attention_rows, decode_allowed, kv_head, merge_partials, softmax_matrix,
+)
 from .brute import attention_brute  # noqa: F401

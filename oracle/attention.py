@@ -26,7 +26,8 @@ LSE_i = log(sum_{j allowed} exp(s_ij)), computed stably as m_i + log(l_i).
 """
 import numpy as np
 
-__all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention", "kv_head"]
+__all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention", "kv_head", "decode_allowed", "attention_decode",
+           "merge_partials"]
 
 
 def _f64(x):
@@ -129,4 +130,79 @@ def attention(q, k, v, scale, causal=False, seqlens=None, row_block=2048):
             for r0 in range(0, N, row_block):
                 rows = np.arange(r0, min(N, r0 + row_block))
                 o[b, h, rows], lse[b, h, rows] = attention_rows(q, k, v, scale, causal, seqlens, b, h, rows)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------------
+# Decoding: a few new queries against a long key/value cache.
+# ---------------------------------------------------------------------------------
+def decode_allowed(n_q, n_keys, valid_len, causal):
+    """Boolean [n_q, n_keys] mask of the decode problem.
+
+    The pages mention inference kernels built on the same method (FlashAttention
+    (UR), section on specialised solutions) without defining their masks.  The
+    reading used here: batch b holds valid_len valid keys (positions
+    0 .. valid_len-1, the cache); its n_q queries are the LAST n_q positions of
+    that sequence, query i at position valid_len - n_q + i.  Every query sees
+    the valid keys; causal additionally drops keys after its own position
+    (j <= valid_len - n_q + i).  With n_q = n_keys = valid_len this is the
+    causal mask of ``attention``.
+    """
+    i = np.arange(n_q, dtype=np.int64)[:, None]
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    allowed = np.broadcast_to(j < valid_len, (n_q, n_keys)).copy()
+    if causal:
+        allowed &= j <= valid_len - n_q + i
+    return allowed
+
+
+def attention_decode(q, k, v, scale, causal=False, seqlens=None):
+    """O [B, H, Nq, d] and LSE [B, H, Nq] of the decode problem, float64.
+
+    q is [B, H, Nq, d]; k and v are [B, H_kv, Nk, d] (H_kv divides H, see
+    ``kv_head``); seqlens [B] gives each batch's valid cache length (clamped to
+    [0, Nk]; None = Nk).  The softmax is the definition itself: S in full, row
+    max shift, normalised weights, rows with no key give O = 0, LSE = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    o = np.zeros((B, H, Nq, v.shape[3]))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        L = _valid_len(seqlens, b, Nk)
+        allowed = decode_allowed(Nq, Nk, L, causal)
+        nonempty = allowed.any(axis=1)
+        for h in range(H):
+            g = kv_head(h, H, k.shape[1])
+            s = float(scale) * (q[b, h] @ k[b, g].T)
+            m = np.where(allowed, s, -np.inf).max(axis=1, initial=-np.inf)
+            shift = np.where(nonempty, m, 0.0)
+            w = np.where(allowed, np.exp(np.where(allowed, s, 0.0) - shift[:, None]), 0.0)
+            l = w.sum(axis=1)
+            p = np.divide(w, l[:, None], out=np.zeros_like(w), where=nonempty[:, None])
+            o[b, h] = p @ v[b, g]
+            lse[b, h, nonempty] = m[nonempty] + np.log(l[nonempty])
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention over disjoint key sets: o_parts [..., S, d], lse_parts [..., S].
+
+    For partial results O_s = softmax over key set s, LSE_s = log sum over set s,
+    the result over the union is LSE = log sum_s exp(LSE_s) and
+    O = sum_s exp(LSE_s - LSE) O_s (the online-softmax combination of
+    FlashAttention (UR), section "Online computation of softmax", applied to
+    whole partial results).  Sets with LSE_s = -inf contribute nothing; if all
+    are empty, O = 0 and LSE = -inf.
+    """
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    m = lse_parts.max(axis=-1)
+    finite = np.isfinite(m)
+    mm = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - mm[..., None]), 0.0)
+    tot = w.sum(axis=-1)
+    lse = np.where(finite, mm + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    o = np.einsum("...s,...sd->...d", np.divide(w, np.where(finite, tot, 1.0)[..., None]), o_parts)
     return o, lse

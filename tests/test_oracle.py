@@ -288,3 +288,88 @@ def test_head_counts_must_divide():
     k = np.zeros((1, 3, 3, 2))
     with pytest.raises(ValueError):
         attention(q, k, k, 1.0)
+
+
+# ---------------------------------------------------------------------------------
+# Decoding against a key/value cache, and the merge of partial results.
+# ---------------------------------------------------------------------------------
+def _brute_decode(q, k, v, scale, causal, seqlens):
+    """Row by row with math.exp / math.fsum and no max shift: query i of batch b
+    sees key j iff j < L_b and (not causal or j <= L_b - Nq + i)."""
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    o = np.zeros((B, H, Nq, v.shape[3]))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        L = Nk if seqlens is None else min(max(int(seqlens[b]), 0), Nk)
+        for h in range(H):
+            g = h // (H // Hkv)
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if j < L and (not causal or j <= L - Nq + i)]
+                if not keys:
+                    continue
+                w = [math.exp(scale * math.fsum(q[b, h, i, c] * k[b, g, j, c] for c in range(d))) for j in keys]
+                tot = math.fsum(w)
+                o[b, h, i] = [math.fsum(wj * v[b, g, j, c] for wj, j in zip(w, keys)) / tot for c in range(v.shape[3])]
+                lse[b, h, i] = math.log(tot)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk,H,Hkv", [(1, 9, 2, 2), (3, 9, 4, 2), (4, 4, 2, 1), (5, 11, 3, 1)])
+def test_decode_matches_brute_force(Nq, Nk, H, Hkv, causal):
+    rng = np.random.default_rng(Nq * 100 + Nk)
+    B, d = 3, 4
+    q = rng.normal(size=(B, H, Nq, d))
+    k = rng.normal(size=(B, Hkv, Nk, d))
+    v = rng.normal(size=(B, Hkv, Nk, 2))
+    for seqlens in (None, np.array([0, 2, Nk])):
+        o, lse = oracle.attention_decode(q, k, v, 0.6, causal, seqlens)
+        o_ref, lse_ref = _brute_decode(q, k, v, 0.6, causal, seqlens)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_decode_agrees_with_full_attention():
+    # Nq = Nk = L: the decode causal mask is the ordinary causal mask; Nq = 1 on the
+    # whole cache is the last row of causal (and of non-causal) attention.
+    rng = np.random.default_rng(3)
+    q = rng.normal(size=(2, 2, 6, 3))
+    k = rng.normal(size=(2, 2, 6, 3))
+    v = rng.normal(size=(2, 2, 6, 3))
+    o, lse = oracle.attention_decode(q, k, v, 0.8, True)
+    o2, lse2 = attention(q, k, v, 0.8, True)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-13)
+    o1, l1 = oracle.attention_decode(q[:, :, -1:], k, v, 0.8, True)
+    np.testing.assert_allclose(o1[:, :, 0], o2[:, :, -1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1[:, :, 0], lse2[:, :, -1], rtol=0, atol=1e-13)
+
+
+def test_decode_causal_mask_is_bottom_aligned():
+    m = oracle.decode_allowed(2, 6, 5, True)
+    assert m.tolist() == [[True, True, True, True, False, False], [True, True, True, True, True, False]]
+    assert not oracle.decode_allowed(3, 6, 1, True)[0].any()   # query before the first key: empty row
+
+
+@pytest.mark.parametrize("splits", [[0, 4, 9], [0, 1, 2, 9], [0, 9], [0, 3, 3, 9]])
+def test_merge_of_key_chunks_is_the_whole(splits):
+    # attention over key chunks [a, b), merged, equals attention over all keys
+    rng = np.random.default_rng(len(splits))
+    q = rng.normal(size=(1, 2, 3, 4))
+    k = rng.normal(size=(1, 2, 9, 4))
+    v = rng.normal(size=(1, 2, 9, 5))
+    parts_o, parts_l = [], []
+    for a, b in zip(splits[:-1], splits[1:]):
+        o, l = oracle.attention_decode(q, k[:, :, a:b], v[:, :, a:b], 0.5, False)
+        parts_o.append(o)
+        parts_l.append(l)
+    om, lm = oracle.merge_partials(np.stack(parts_o, axis=-2), np.stack(parts_l, axis=-1))
+    o_ref, l_ref = _brute_decode(q, k, v, 0.5, False, None)
+    np.testing.assert_allclose(om, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, l_ref, rtol=0, atol=1e-12)
+
+
+def test_merge_of_empty_parts():
+    o, l = oracle.merge_partials(np.zeros((2, 3, 4)), np.full((2, 3), -np.inf))
+    assert np.all(o == 0) and np.all(l == -np.inf)

@@ -38,7 +38,8 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s (bf16, 1 GPU) and % of MFMA bf16 dense peak"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["exact_io_aware_57_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_57_amd/csrc/fa_internal.h"]
+KERNEL_SOURCES = ["exact_io_aware_57_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_57_amd/csrc/fa_device.h",
+                  "exact_io_aware_57_amd/csrc/fa_internal.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -191,6 +192,41 @@ def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=T
             "frac_of_bf16_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def time_decode(dev, stream_handle, B=8, H=32, H_kv=8, Nq=1, Nk=32768, d=128, causal=True, std=0.5, seed=7, steps=50):
+    """Time of one fa_decode call (key-split kernel + merge kernel) on seeded
+    inputs: Nq new queries per head against a full cache of Nk keys.  The step
+    reads the cache once, so it is priced against HBM bandwidth with its
+    compulsory bytes (K and V of the valid keys, Q, O and LSE)."""
+    import torch
+
+    from exact_io_aware_57_amd import binding
+    from exact_io_aware_57_amd.inputs import random_decode
+
+    q, k, v, _ = random_decode(B, H, H_kv, Nq, Nk, d, torch.bfloat16, std, seed)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    need = binding.fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+    def launch():
+        st = binding.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, Nq,
+                               Nk, d, scale, causal, None, 0, ws.data_ptr(), need, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"fa_decode failed: {binding.fa_status_str(st)}")
+
+    m_step, m_kern, m_min = time_launches(launch, steps, 10)
+    cbytes = 2 * B * H_kv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+    splits = need // (B * H * Nq * (d + 1) * 4)
+    return {"workload": f"decode: B={B} H={H} H_kv={H_kv} Nq={Nq} cache={Nk} d={d} bf16 "
+                        f"{'causal' if causal else 'non-causal'}, {splits} key splits",
+            "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5), "kernel_ms_min": round(m_min, 5),
+            "compulsory_bytes": cbytes, "workspace_bytes": need,
+            "hbm_gbs_compulsory": round(cbytes / (m_kern * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(cbytes / (m_kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(index, heads):
     """The oracle as it stands on `heads` whole heads of the workload."""
     import numpy as np
@@ -336,6 +372,8 @@ def main(argv=None):
         # grouped-query variant of the long-context shape (8 key/value heads
         # shared by groups of 4 query heads): same FLOP, a quarter of the K/V
         others["long_context_gqa"] = time_grouped(dev, stream.cuda_stream)
+        # one decode step against a long key/value cache (HBM-bound)
+        others["decode"] = time_decode(dev, stream.cuda_stream)
 
     traffic = read_traffic(wl.name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),

@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the attention forward pass runs in the
 HIP kernels of libfa_mi355x.so.  ``fa_fwd``, ``fa_fwd_f32`` and
-``fa_fwd_gqa``, ``fa_fwd_gqa_f32`` and ``fa_status_str`` mirror the C entry points one to one (raw device pointers as
+``fa_fwd_gqa``, ``fa_fwd_gqa_f32``, ``fa_decode``, ``fa_decode_workspace_size`` and ``fa_status_str`` mirror
+the C entry points one to one (raw device pointers as
 ints, a hipStream_t as an int or None).  ``attention_forward`` is a convenience
 wrapper for torch device tensors: it checks shapes, dtypes and layout, takes
 the pointers and the current stream, and raises ``FaError`` on a non-zero
@@ -21,7 +22,8 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_NO_DEVICE = -4
 FA_ERR_LAUNCH = -5
 
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32",
+                    "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +59,10 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
             fn.restype = i32
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, ctypes.c_size_t, vp]
+        lib.fa_decode.restype = i32
+        lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_status_str.argtypes = [i32]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -89,6 +95,51 @@ def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, seqlens, st
     """C fa_fwd_gqa_f32 with integer device pointers (k, v have H_kv heads)."""
     return load().fa_fwd_gqa_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
                                  float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, workspace, workspace_size,
+              stream):
+    """C fa_decode with integer device pointers."""
+    return load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(Nq), int(Nk),
+                            int(d), float(scale), int(bool(causal)), _ptr(seqlens), int(num_splits), _ptr(workspace),
+                            int(workspace_size), _ptr(stream))
+
+
+def fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits=0):
+    """Bytes of workspace fa_decode needs (0 for invalid arguments)."""
+    return int(load().fa_decode_workspace_size(int(B), int(H), int(H_kv), int(Nq), int(Nk), int(d), int(num_splits)))
+
+
+def decode_forward(q, k, v, scale, causal=False, seqlens=None, num_splits=0, out=None, lse=None, workspace=None,
+                   stream=None, want_lse=True):
+    """O (and LSE) of a decode step for torch bf16 device tensors q [B, H, Nq, d]
+    and k, v [B, H_kv, Nk, d].  The workspace (a uint8 device tensor) is
+    allocated with torch when not given.  Returns (out, lse or None)."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"need q [B, H, Nq, d] and k, v [B, H_kv, Nk, d], got {tuple(q.shape)}, {tuple(k.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16) or not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be bfloat16 device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+                   B, H, H_kv, Nq, Nk, d, scale, causal, None if seqlens is None else seqlens.data_ptr(), num_splits,
+                   workspace.data_ptr(), workspace.numel(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+    return out, lse
 
 
 def fa_status_str(status):

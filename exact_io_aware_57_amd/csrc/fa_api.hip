@@ -66,9 +66,67 @@ int run(const fa::FwdParams& p, void* stream, bool bf16) {
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Key splits of a decode problem: enough workgroups to cover the chip twice,
+// at least 4 tiles per split, at most 128 splits.
+int decode_splits(int B, int H, int H_kv, int Nq, int Nk, int requested) {
+  if (requested > 0) return requested;
+  const long long rows = (long long)(H / H_kv) * Nq;
+  const long long qblk = (rows + fa::decode_rows_per_block() - 1) / fa::decode_rows_per_block();
+  const long long base = (long long)B * H_kv * qblk;
+  const long long tiles = ((long long)Nk + fa::decode_tile_keys() - 1) / fa::decode_tile_keys();
+  long long s = (512 + base - 1) / base;
+  const long long s_max = tiles / 4 > 1 ? tiles / 4 : 1;
+  if (s > s_max) s = s_max;
+  if (s > 128) s = 128;
+  return (int)(s < 1 ? 1 : s);
+}
+
+bool decode_shape_ok(int B, int H, int H_kv, int Nq, int Nk, int d) {
+  return B >= 1 && H >= 1 && Nq >= 1 && Nk >= 1 && H_kv >= 1 && H_kv <= H && H % H_kv == 0 && (d == 64 || d == 128);
+}
+
+size_t workspace_bytes(int B, int H, int Nq, int d, int S) {
+  const size_t rows = (size_t)B * H * Nq;
+  return rows * (size_t)S * (size_t)d * sizeof(float) + rows * (size_t)S * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits) {
+  if (!decode_shape_ok(B, H, H_kv, Nq, Nk, d) || num_splits < 0) return 0;
+  return workspace_bytes(B, H, Nq, d, decode_splits(B, H, H_kv, Nq, Nk, num_splits));
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              const int32_t* seqlens, int num_splits, void* workspace, size_t workspace_size, void* stream) {
+  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || num_splits < 0)
+    return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * H * Nq * d > (uint64_t(1) << 40) || (uint64_t)B * H_kv * Nk * d > (uint64_t(1) << 40))
+    return FA_ERR_INVALID_ARG;
+  const int S = decode_splits(B, H, H_kv, Nq, Nk, num_splits);
+  const long long rows = (long long)(H / H_kv) * Nq;
+  const long long qblk = (rows + fa::decode_rows_per_block() - 1) / fa::decode_rows_per_block();
+  if ((long long)B * H_kv * qblk * S > INT32_MAX || (long long)B * H * Nq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (workspace_size < workspace_bytes(B, H, Nq, d, S)) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16))
+    return FA_ERR_MISALIGNED;
+  if (lse && !aligned(lse, 4)) return FA_ERR_MISALIGNED;
+  if (seqlens && !aligned(seqlens, 4)) return FA_ERR_MISALIGNED;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  const size_t orows = (size_t)B * H * Nq;
+  float* opart = reinterpret_cast<float*>(workspace);
+  float* lpart = opart + orows * (size_t)S * (size_t)d;
+  fa::DecodeParams p{q, k, v, o, lse, seqlens, opart, lpart, B, H, H_kv, Nq, Nk, d, scale, causal ? 1 : 0, S, (int)qblk};
+  return fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,

@@ -47,99 +47,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
-constexpr float kMaxTileSum = 256.0f;   // 2^kTau
-
-template <int D, int BN>
-struct Tile {
-  static constexpr int KB = BN / 32;                // 32-key blocks per tile
-  static constexpr int CH = D / 8;                  // 16-byte chunks per row
-  static constexpr int DC = D / 16;                 // k-steps of S^T = K Q^T
-  static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  static constexpr int ROW = D * 2;                 // bytes per row
-  static constexpr int MAT = BN * ROW;              // one K or V tile
-  static constexpr int STAGE = 2 * MAT;             // K + V
-  static constexpr int NLD = MAT / (1024 * kWaves); // 1 KB wave-loads per wave per matrix
-  static_assert(MAT % (1024 * kWaves) == 0, "tile load must split evenly over the waves");
-};
-
-// LDS swizzles (16-byte chunk c of row r is stored at chunk c ^ swz(r)), chosen
-// by measurement on gfx950, where ds_read_b128 is serviced 16 lanes (256 bytes)
-// at a time and ds_read_b64_tr_b16 32 lanes at a time.
-// K: the S^T A-operand read sends 16 consecutive rows, same chunk, through one
-// cycle; the XOR spreads them over all 64 banks (d=64 rows are 128 bytes, so
-// two rows share a 256-byte bank line).
-template <int D>
-__device__ __forceinline__ int kswz(int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); }
-// V: 16 lanes of the transposing read cover 4 consecutive rows x 32 bytes, 32
-// lanes 4 rows x 64 bytes; an XOR by a multiple of 2 chunks keeps each 32-byte
-// pair together and places the 4 rows in distinct banks.
-template <int D>
-__device__ __forceinline__ int vswz(int row) { return D == 64 ? ((row & 3) << 1) : ((row & 3) << 2); }
-
-// Value of x from the other half-wave (lane ^ 32) combined with x.  The
-// permlane32 swap exchanges the two half-waves between its two results, so one
-// of the pair is x and the other the partner's value in every lane.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  bf16x2 v;
-  v[0] = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// An empty volatile asm: marks a rarely taken branch (the softmax rescale) so
-// that the compiler keeps it a branch instead of executing its body on every
-// tile with a neutral factor.
-__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
-
-// Empty volatile asm that consumes a register value: the computation of the
-// value cannot be moved after this point (register-only arithmetic may
-// otherwise migrate across a workgroup barrier, which orders memory only).
-template <typename V>
-__host__ __device__ __forceinline__ void pin(const V& v) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("" ::"v"(v));
-#endif
-}
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes lds_base + 16 i (global_load_lds_dwordx4).  The builtin exists only for
-// the device target; clang's host pass drops a kernel whose body names it, so
-// its use is confined to the device pass.
-__device__ __forceinline__ void load_to_lds16(const void* src, void* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
-#endif
-}
 
 template <int D, int QB, int BN, int OCC, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
@@ -433,16 +345,6 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
 // at the end of phase 2t+1, before any wave reads them.
 // ---------------------------------------------------------------------------
 
-// 16 bytes per lane from global memory straight into LDS (lane i of the wave to
-// lds_base + 16 i).  Issued as inline assembly so that the compiler does not
-// treat the LDS buffers being filled as aliasing the ones being read; the
-// kernel waits for these loads itself (vmcnt) before the barrier that publishes
-// them.  M0 carries the LDS base; the s_nop is the wait state the hardware
-// requires between an M0 write and its use by an LDS DMA.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  const unsigned l = (unsigned)(uintptr_t)((lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src) : "memory", "m0");
-}
 
 template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {

@@ -111,6 +111,23 @@ def random_qkv_grouped(B, H, H_kv, N, d, dtype=torch.bfloat16, std=1.0, seed=0, 
     return out[0], out[1], out[2], seqlens
 
 
+def random_decode(B, H, H_kv, Nq, Nk, d, dtype=torch.bfloat16, std=1.0, seed=0, len_range=None):
+    """Decode inputs: Q [B, H, Nq, d] and the cache K, V [B, H_kv, Nk, d] as CPU
+    tensors (+ per-batch cache lengths drawn from len_range, or None), all from
+    one seeded generator in that order."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = []
+    for shape in ((B, H, Nq, d), (B, H_kv, Nk, d), (B, H_kv, Nk, d)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        out.append(x.to(dtype).contiguous())
+    seqlens = None
+    if len_range is not None:
+        seqlens = random_seqlens(B, len_range[0], len_range[1], g)
+    return out[0], out[1], out[2], seqlens
+
+
 def make_inputs(index, seed=None):
     """Inputs of a numbered workload: dict(q, k, v, seqlens, scale, causal, wl).
 

@@ -44,6 +44,7 @@
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -103,6 +104,38 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int B, int H, int H_kv, int N, int d, float scale, int causal,
                    const int32_t* seqlens, void* stream);
+
+/*
+ * Decoding against a key/value cache, keys split across workgroups.
+ *   q, o     : [B, H, Nq, d] bf16 (Nq new queries per head), o written
+ *   k, v     : [B, H_kv, Nk, d] bf16 (the cache; H_kv divides H, grouped as
+ *              in fa_fwd_gqa)
+ *   lse      : float [B, H, Nq] output, natural log; may be NULL
+ *   seqlens  : int32 [B] valid cache length per batch on the device (clamped
+ *              to [0, Nk]), or NULL for Nk
+ *   causal   : query i of batch b is position L_b - Nq + i of its sequence
+ *              and sees only keys j <= L_b - Nq + i (non-zero), or every
+ *              valid key (0)
+ *   num_splits : key chunks per (batch, key/value head); 0 = chosen by the
+ *              library from the shape
+ *   workspace, workspace_size : caller-owned device memory of at least
+ *              fa_decode_workspace_size(...) bytes (16-byte aligned), used for
+ *              the partial results; its contents on entry do not matter
+ * The keys of each valid cache are split into num_splits contiguous chunks of
+ * whole 64-key tiles; one kernel computes each chunk's softmax average and
+ * log-sum-exp, a second kernel combines the chunks (LSE = log sum exp LSE_s,
+ * O = sum exp(LSE_s - LSE) O_s; FlashAttention (UR), section "Online
+ * computation of softmax", applied to whole partial results).  Arithmetic as
+ * fa_fwd; partial results are float32.  Returns FA_OK or a negative fa_status
+ * (FA_ERR_INVALID_ARG also for a workspace smaller than required); nothing is
+ * enqueued on error.
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+              const int32_t* seqlens, int num_splits, void* workspace, size_t workspace_size, void* stream);
+
+/* Bytes of workspace fa_decode needs for these arguments (0 for invalid ones). */
+size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);

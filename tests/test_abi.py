@@ -30,7 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
+    assert declared_functions() == ["fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_gqa",
+                                    "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -132,3 +133,40 @@ def test_grouped_head_counts_are_checked_on_the_host(lib, fn):
     assert call_gqa(fn, q=None) == E.FA_ERR_INVALID_ARG
     assert call_gqa(fn, d=96) == E.FA_ERR_UNSUPPORTED
     assert call_gqa(fn, k=FAKE + 4) == E.FA_ERR_MISALIGNED
+
+
+DEC = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, H=8, H_kv=2, Nq=1, Nk=1000, d=128, scale=0.1, causal=0,
+           seqlens=None, num_splits=0, workspace=FAKE, workspace_size=1 << 30, stream=None)
+
+
+def call_dec(**over):
+    a = dict(DEC)
+    a.update(over)
+    return binding.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"], a["Nq"], a["Nk"], a["d"],
+                             a["scale"], a["causal"], a["seqlens"], a["num_splits"], a["workspace"], a["workspace_size"],
+                             a["stream"])
+
+
+def test_decode_workspace_size(lib):
+    f = binding.fa_decode_workspace_size
+    # rows * splits * (d + 1) floats
+    assert f(2, 8, 2, 1, 1000, 128, 3) == 2 * 8 * 1 * 3 * 129 * 4
+    assert f(1, 1, 1, 4, 64, 64, 1) == 4 * 65 * 4
+    auto = f(2, 8, 2, 1, 100000, 128, 0)
+    assert auto > 0 and auto % (2 * 8 * 129 * 4) == 0
+    for bad in [dict(H_kv=3), dict(d=96), dict(Nq=0), dict(Nk=0), dict(num_splits=-1)]:
+        a = dict(B=2, H=8, H_kv=2, Nq=1, Nk=1000, d=128, num_splits=0)
+        a.update(bad)
+        assert f(**a) == 0, bad
+
+
+def test_decode_arguments_are_checked_on_the_host(lib):
+    E = binding
+    for name in ("q", "k", "v", "o", "workspace"):
+        assert call_dec(**{name: None}) == E.FA_ERR_INVALID_ARG, name
+    for over in (dict(B=0), dict(Nq=0), dict(Nk=-1), dict(H_kv=3), dict(H_kv=16), dict(num_splits=-2), dict(scale=0.0),
+                 dict(workspace_size=16)):
+        assert call_dec(**over) == E.FA_ERR_INVALID_ARG, over
+    assert call_dec(d=256) == E.FA_ERR_UNSUPPORTED
+    assert call_dec(workspace=FAKE + 4) == E.FA_ERR_MISALIGNED
+    assert call_dec(q=FAKE + 8) == E.FA_ERR_MISALIGNED

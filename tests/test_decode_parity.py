@@ -1,0 +1,197 @@
+"""GPU parity of the split-key decode path (fa_decode) against the float64 oracle.
+
+The decode step: Nq new queries per (batch, head) against a cache of K/V with
+per-batch valid lengths; query i sits at position L - Nq + i (oracle
+``decode_allowed``).  The keys are split into chunks whose partial (O, LSE)
+pairs are merged; the result must equal the softmax over all keys.
+
+Tolerances are those of the bf16 forward pass: max-abs <= 1e-2 on O, mean-abs
+<= 1e-3 against the oracle rounded to bf16, LSE max-abs <= 2.5e-3 (the
+partial results are held in float32, so the merge adds only float32 rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_57_amd import binding
+from exact_io_aware_57_amd.inputs import random_decode
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, BF16_LSE = 1e-2, 1e-3, 2.5e-3
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def np64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def gpu_decode(q, k, v, scale, causal, seqlens, num_splits=0, want_lse=True, workspace=None):
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    sd = None if seqlens is None else seqlens.to(DEV)
+    o, lse = binding.decode_forward(qd, kd, vd, scale, causal, sd, num_splits=num_splits, want_lse=want_lse,
+                                    workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(q, k, v, scale, causal, seqlens, tag, num_splits=0):
+    B, H, Nq, d = q.shape
+    H_kv, Nk = k.shape[1], k.shape[2]
+    S = binding.fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits) // (B * H * Nq * (d + 1) * 4)
+    say(f"[decode] {tag}: B={B} H={H} H_kv={H_kv} Nq={Nq} Nk={Nk} d={d} causal={causal} "
+        f"seqlens={None if seqlens is None else seqlens.tolist()} splits={S}")
+    o, lse = gpu_decode(q, k, v, scale, causal, seqlens, num_splits)
+    o_ref, lse_ref = oracle.attention_decode(np64(q), np64(k), np64(v), scale, causal,
+                                             None if seqlens is None else seqlens.numpy())
+    og, lg = np64(o), np64(lse)
+    assert np.isfinite(og).all(), "non-finite output"
+    err = np.abs(og - o_ref)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lg), fin), "LSE -inf pattern differs"
+    assert np.all(lg[~fin] == -np.inf)
+    assert np.all(og[~fin] == 0.0), "rows with no key must be zero"
+    lerr = np.abs(lg[fin] - lse_ref[fin]).max() if fin.any() else 0.0
+    rounded = torch.from_numpy(o_ref).to(torch.bfloat16).double().numpy()
+    err_r = np.abs(og - rounded)
+    say(f"[decode] {tag}: O max {err.max():.3e} mean vs bf16-rounded {err_r.mean():.3e}  LSE max {lerr:.3e}")
+    assert err.max() <= BF16_MAX
+    assert err_r.mean() <= BF16_MEAN
+    assert lerr <= BF16_LSE
+    return og, lg
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv,Nq", [(8, 8, 1), (8, 2, 1), (8, 2, 4), (6, 1, 16)])
+def test_decode_parity(H, H_kv, Nq, d, causal):
+    q, k, v, sl = random_decode(3, H, H_kv, Nq, 1000, d, seed=11 + Nq + H_kv, len_range=(1, 1000))
+    check(q, k, v, d ** -0.5, causal, sl, f"H{H}/{H_kv} Nq{Nq}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 0])
+def test_decode_split_counts(num_splits):
+    """Every key split (one chunk, uneven chunks, more chunks than tiles would
+    fill, the automatic choice) gives the oracle's answer."""
+    q, k, v, sl = random_decode(2, 8, 2, 3, 1337, 128, seed=5, len_range=(200, 1337))
+    check(q, k, v, 128 ** -0.5, True, sl, f"splits {num_splits}", num_splits=num_splits)
+
+
+def test_decode_more_splits_than_tiles():
+    """Splits beyond the tile count are empty (LSE -inf) and drop out of the merge."""
+    q, k, v, _ = random_decode(1, 4, 4, 2, 130, 64, seed=6)
+    check(q, k, v, 0.125, False, None, "splits > tiles", num_splits=9)
+
+
+def test_decode_short_and_empty_caches():
+    """Cache lengths 0, 1, below Nq, one tile, one tile + 1: causal rows whose
+    position is negative see no key and give O = 0, LSE = -inf."""
+    q, k, v, _ = random_decode(6, 4, 2, 5, 200, 128, seed=7)
+    sl = torch.tensor([0, 1, 3, 64, 65, 200], dtype=torch.int32)
+    for causal in (False, True):
+        check(q, k, v, 128 ** -0.5, causal, sl, f"short caches causal={causal}")
+
+
+def test_decode_tiny_cache():
+    for nk in (1, 7, 63, 64, 65):
+        q, k, v, _ = random_decode(2, 4, 1, 2, nk, 64, seed=nk)
+        check(q, k, v, 0.125, True, None, f"Nk={nk}")
+
+
+@pytest.mark.parametrize("H,H_kv,Nq", [(32, 1, 8), (24, 1, 7), (64, 8, 20)])
+def test_decode_many_query_rows(H, H_kv, Nq):
+    """More than 128 query rows per key/value head: several row blocks, the
+    last one ragged."""
+    q, k, v, sl = random_decode(2, H, H_kv, Nq, 777, 128, seed=H + Nq, len_range=(100, 777))
+    check(q, k, v, 128 ** -0.5, True, sl, f"rows {H // H_kv * Nq}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_long_cache(d):
+    """A long cache (32768 keys, lengths ragged across the batch), Nq = 1, grouped
+    heads: the automatic split count is large here."""
+    q, k, v, sl = random_decode(2, 32, 8, 1, 32768, d, seed=21, len_range=(20000, 32768))
+    check(q, k, v, d ** -0.5, True, sl, "long cache")
+
+
+def test_decode_equals_causal_forward():
+    """Nq = Nk = L: the decode problem is the causal forward pass."""
+    q, k, v, _ = random_decode(2, 4, 4, 300, 300, 64, seed=8)
+    od, ld = gpu_decode(q, k, v, 0.125, True, None, num_splits=2)
+    of, lf = binding.attention_forward(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, True, None)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(np64(q), np64(k), np64(v), 0.125, True)
+    for o, lse in ((od, ld), (of, lf)):
+        assert np.abs(np64(o) - o_ref).max() <= BF16_MAX
+        assert np.abs(np64(lse) - lse_ref).max() <= BF16_LSE
+    assert np.abs(np64(od) - np64(of)).max() <= 2 * BF16_MAX
+
+
+def test_decode_split_counts_agree():
+    """Different key splits give the same answer to within the oracle bounds.
+    They are not just float32 summation orders of one another: each chunk
+    rounds its probabilities to bf16 relative to its own running max, so each
+    split count carries its own rounding of l (each LSE within ln(1 + 2^-9) of
+    the exact one); two split counts therefore agree within twice the bounds."""
+    q, k, v, sl = random_decode(2, 16, 4, 2, 4096, 128, seed=9, len_range=(3000, 4096))
+    outs = [gpu_decode(q, k, v, 128 ** -0.5, False, sl, num_splits=s) for s in (1, 4, 16, 64)]
+    o0, l0 = np64(outs[0][0]), np64(outs[0][1])
+    for o, lse in outs[1:]:
+        assert np.abs(np64(o) - o0).max() <= 2 * BF16_MAX
+        assert np.abs(np64(lse) - l0).max() <= 2 * BF16_LSE
+
+
+def test_decode_lse_optional_deterministic_and_workspace_reuse():
+    q, k, v, sl = random_decode(2, 8, 2, 4, 2000, 128, seed=10, len_range=(500, 2000))
+    need = binding.fa_decode_workspace_size(2, 8, 2, 4, 2000, 128, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o1, l1 = gpu_decode(q, k, v, 0.1, True, sl, workspace=ws)
+    o2, l2 = gpu_decode(q, k, v, 0.1, True, sl, workspace=ws)
+    o3, l3 = gpu_decode(q, k, v, 0.1, True, sl, want_lse=False, workspace=ws)
+    assert l3 is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
+    # a smaller problem in the same (larger) workspace
+    qs, ks, vs, _ = random_decode(1, 4, 1, 1, 100, 128, seed=12)
+    o_s, l_s = gpu_decode(qs, ks, vs, 0.1, False, None, workspace=ws)
+    o_ref, lse_ref = oracle.attention_decode(np64(qs), np64(ks), np64(vs), 0.1, False)
+    assert np.abs(np64(o_s) - o_ref).max() <= BF16_MAX
+    assert np.abs(np64(l_s) - lse_ref).max() <= BF16_LSE
+
+
+def test_decode_guard_bands_untouched():
+    """The kernels write exactly B*H*Nq*d outputs and B*H*Nq LSE values."""
+    q, k, v, sl = random_decode(2, 8, 2, 3, 500, 64, seed=13, len_range=(1, 500))
+    B, H, Nq, d = q.shape
+    n = B * H * Nq * d
+    obuf = torch.full((n + 256,), 7.0, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((B * H * Nq + 64,), 7.0, dtype=torch.float32, device=DEV)
+    out = obuf[:n].view(B, H, Nq, d)
+    lse = lbuf[:B * H * Nq].view(B, H, Nq)
+    binding.decode_forward(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, True, sl.to(DEV), out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[n:] == 7.0) and torch.all(lbuf[B * H * Nq:] == 7.0)
+
+
+def test_decode_non_default_stream():
+    q, k, v, sl = random_decode(2, 8, 8, 1, 3000, 128, seed=14, len_range=(1000, 3000))
+    s = torch.cuda.Stream(device=DEV)
+    qd, kd, vd, sd = q.to(DEV), k.to(DEV), v.to(DEV), sl.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o, lse = binding.decode_forward(qd, kd, vd, 0.125, False, sd, stream=s.cuda_stream)
+    s.synchronize()
+    o_ref, _ = oracle.attention_decode(np64(q), np64(k), np64(v), 0.125, False, sl.numpy())
+    assert np.abs(np64(o) - o_ref).max() <= BF16_MAX
+
+
+def test_decode_rejects_small_workspace_on_device():
+    q, k, v, _ = random_decode(1, 4, 4, 1, 1000, 64, seed=15)
+    need = binding.fa_decode_workspace_size(1, 4, 4, 1, 1000, 64, 0)
+    ws = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(binding.FaError):
+        binding.decode_forward(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, False, None, workspace=ws)

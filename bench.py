@@ -165,7 +165,8 @@ def time_launches(launch, steps, warmup):
     return (t1 - t0) * 1e3 / steps, sum(per_launch) / len(per_launch), min(per_launch)
 
 
-def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=True, std=0.5, seed=6, steps=20):
+def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=True, std=0.5, seed=6, steps=20,
+                 name="long_context_gqa"):
     """Kernel time of fa_fwd_gqa on seeded inputs of the given shape."""
     import torch
 
@@ -186,7 +187,7 @@ def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=T
 
     m_step, m_kern, _ = time_launches(launch, steps, 10)
     flops = algorithmic_flops(B, H, N, d, causal)
-    return {"workload": f"long_context_gqa: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 {'causal' if causal else 'non-causal'}",
+    return {"workload": f"{name}: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 {'causal' if causal else 'non-causal'}",
             "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
             "tflops": round(flops / (m_kern * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -372,6 +373,9 @@ def main(argv=None):
         # grouped-query variant of the long-context shape (8 key/value heads
         # shared by groups of 4 query heads): same FLOP, a quarter of the K/V
         others["long_context_gqa"] = time_grouped(dev, stream.cuda_stream)
+        # head size 256 at the long-context size (same FLOP as H = 32, d = 128)
+        others["long_context_d256"] = time_grouped(dev, stream.cuda_stream, H=16, H_kv=16, d=256, seed=8,
+                                                   name="long_context_d256")
         # one decode step against a long key/value cache (HBM-bound)
         others["decode"] = time_decode(dev, stream.cuda_stream)
 

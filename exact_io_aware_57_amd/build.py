@@ -28,10 +28,18 @@ DEVICE_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA results in ordinary VGPRs: the softmax reads every score, and
-    # AGPR-resident accumulators would cost a v_accvgpr move per element
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
+# Keep MFMA results in ordinary VGPRs: the softmax reads every score, and
+# AGPR-resident accumulators would cost a v_accvgpr move per element.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# Sources whose kernels run one wave per SIMD and need the accumulation
+# registers as well (head size 256: 64 registers of Q and 128 of O^T per lane).
+AGPR_FORM_SOURCES = {"fa_fwd_bf16_d256.hip"}
+
+
+def device_flags(src):
+    """hipcc flags for one source file."""
+    return DEVICE_FLAGS + ([] if os.path.basename(src) in AGPR_FORM_SOURCES else VGPR_FORM)
 
 
 def hipcc():
@@ -63,7 +71,7 @@ def build_library(verbose=False, jobs=None):
     cc = hipcc()
     srcs = sources()
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    cmds = [[cc, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[cc, *device_flags(s), "-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
     jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -44,7 +44,7 @@ int validate(const fa::FwdParams& p) {
   if (p.B < 1 || p.H < 1 || p.N < 1) return FA_ERR_INVALID_ARG;
   if (p.Hkv < 1 || p.Hkv > p.H || p.H % p.Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(p.scale) || !(p.scale > 0.0f)) return FA_ERR_INVALID_ARG;
-  if (p.d != 64 && p.d != 128) return FA_ERR_UNSUPPORTED;
+  if (p.d != 64 && p.d != 128 && p.d != 256) return FA_ERR_UNSUPPORTED;
   // Every element offset must fit the 64-bit index arithmetic of the kernels and
   // the workgroup count must fit one grid dimension.
   const uint64_t elems = (uint64_t)p.B * (uint64_t)p.H * (uint64_t)p.N * (uint64_t)p.d;
@@ -62,7 +62,7 @@ int run(const fa::FwdParams& p, void* stream, bool bf16) {
   st = check_device();
   if (st != FA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = bf16 ? fa::launch_fwd_bf16(p, s) : fa::launch_fwd_f32(p, s);
+  hipError_t e = !bf16 ? fa::launch_fwd_f32(p, s) : p.d == 256 ? fa::launch_fwd_bf16_d256(p, s) : fa::launch_fwd_bf16(p, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -128,6 +128,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
   if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (p.d == 256) return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
   return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
 }
 

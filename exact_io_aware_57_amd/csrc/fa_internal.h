@@ -44,6 +44,7 @@ struct DecodeParams {
 // HIP error of the launch itself; launch_decode enqueues the split kernel and
 // the merge kernel.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_bf16_d256(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 int decode_rows_per_block();   // query rows per split-kernel workgroup

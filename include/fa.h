@@ -54,7 +54,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* NULL tensor, B/H/N < 1, H_kv not dividing H, bad scale, size overflow */
-  FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, or the current device is not gfx950 */
+  FA_ERR_UNSUPPORTED = -2, /* d not supported by the entry point, or the current device is not gfx950 */
   FA_ERR_MISALIGNED = -3,  /* q, k, v, o not 16-byte aligned, or lse / seqlens not 4-byte aligned */
   FA_ERR_NO_DEVICE = -4,   /* no HIP device is present or current */
   FA_ERR_LAUNCH = -5       /* the HIP runtime refused the kernel launch */
@@ -66,7 +66,7 @@ typedef enum fa_status {
  *   o       : __hip_bfloat16*        [B, H, N, d]   output, round to nearest even
  *   lse     : float*                 [B, H, N]      output; may be NULL (not written)
  *   B, H, N : batch, heads, sequence length (>= 1); queries and keys share N
- *   d       : head dimension, 64 or 128
+ *   d       : head dimension, 64, 128 or 256
  *   scale   : softmax scale (the pages' 1/sqrt(d_k)); finite and > 0
  *   causal  : 0 or non-zero
  *   seqlens : const int32_t* [B] key-padding lengths on the device, or NULL

@@ -79,7 +79,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, fn):
         assert call(fn, **{name: -3}) == E.FA_ERR_INVALID_ARG, name
     for scale in (0.0, -1.0, float("nan"), float("inf")):
         assert call(fn, scale=scale) == E.FA_ERR_INVALID_ARG, scale
-    for d in (0, 32, 96, 256):
+    for d in (0, 32, 96, 192, 512):
         assert call(fn, d=d) == E.FA_ERR_UNSUPPORTED, d
     for name in ("q", "k", "v", "o"):
         assert call(fn, **{name: FAKE + 8}) == E.FA_ERR_MISALIGNED, name

@@ -149,7 +149,7 @@ def test_large_grid_kernel(d, causal):
                        seed=d + causal)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("H,H_kv", [(8, 4), (8, 2), (6, 1)])
 def test_grouped_query_parity(H, H_kv, d, causal):
@@ -174,6 +174,18 @@ def test_grouped_query_large_grid(d, causal):
                            f"grouped large H_kv={H_kv} d={d}", seed=H_kv)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_size_256_large_grid(causal):
+    """Head size 256 on a grid of many workgroups (its own kernel at every size):
+    sampled rows of several heads against the oracle, and bitwise repeatable."""
+    B, H, N = 2, 8, 4096
+    q, k, v, _ = random_qkv(B, H, N, 256, torch.bfloat16, 0.5, seed=90 + causal)
+    check_sampled_rows(q, k, v, 1.0 / 16.0, causal, None, [(0, 0), (1, 3), (1, 7)], "d=256 large", seed=causal)
+    o1, l1 = gpu_forward(q, k, v, 1.0 / 16.0, causal, None)
+    o2, l2 = gpu_forward(q, k, v, 1.0 / 16.0, causal, None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_grouped_query_equals_repeated_heads():
     # the kernel's grouped path against its own plain path on repeated K/V: bitwise equal
     q, k, v, _ = random_qkv_grouped(2, 8, 2, 257, 128, torch.bfloat16, 1.0, seed=9)
@@ -186,7 +198,7 @@ def test_grouped_query_equals_repeated_heads():
 RAGGED_N = [1, 2, 3, 7, 8, 31, 33, 63, 64, 65, 100, 127, 129, 255, 256, 257, 300, 513, 1000]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_lengths_bf16(d, causal):
     for n in RAGGED_N:
@@ -194,7 +206,7 @@ def test_ragged_lengths_bf16(d, causal):
         check_against_oracle(q, k, v, 1.0 / math.sqrt(d), causal, None, fp32=False, tag=f"ragged n={n} d={d}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_padding_lengths_bf16(d, causal):
     n = 300
@@ -213,7 +225,7 @@ def test_padding_lengths_out_of_range_are_clamped():
     assert np.all(np64(lse)[0] == -np.inf) and np.all(np64(o)[0] == 0)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_fp32_path(d):
     for n, causal, lens in [(128, False, None), (1, False, None), (77, True, None), (200, False, [0, 150]),
                             (333, True, [333, 90])]:

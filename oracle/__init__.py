@@ -21,6 +21,8 @@ attention : the definition in numpy float64 (``attention``, ``attention_rows``,
             attention, ``attention_decode`` for a few queries against a key
             cache, ``merge_partials`` for combining results over disjoint key
             sets).  Every function is pinned by tests/test_oracle.py.
+backward  : ``attention_backward``, the gradients dQ, dK, dV of the definition by
+            the chain rule (the pages give no backward algorithm).
 brute     : the same definition as scalar Python loops with ``math.exp`` and
             ``math.fsum`` and no max shift; a second, independent code path used
             only to pin ``attention`` on tiny inputs.
@@ -28,4 +30,5 @@ brute     : the same definition as scalar Python loops with ``math.exp`` and
 from .attention import (  # noqa: F401
     allowed_mask, attention, attention_decode, attention_rows, decode_allowed, kv_head, merge_partials, softmax_matrix,
 )
+from .backward import attention_backward  # noqa: F401
 from .brute import attention_brute  # noqa: F401

@@ -228,6 +228,42 @@ def time_decode(dev, stream_handle, B=8, H=32, H_kv=8, Nq=1, Nk=32768, d=128, ca
             "frac_of_hbm_peak": round(cbytes / (m_kern * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def time_backward(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal=True, std=0.5, seed=9, steps=10):
+    """Time of one fa_bwd call (row-dot, dK/dV and dQ kernels) on seeded
+    inputs; O and LSE come from the forward pass on the same inputs.  FLOP are
+    counted as the five products of the chain rule, 2.5 times the forward
+    pass's (the dQ kernel's recomputation of S and dP is not counted)."""
+    import torch
+
+    from exact_io_aware_57_amd import binding
+    from exact_io_aware_57_amd.inputs import random_qkv_grouped
+
+    q, k, v, _ = random_qkv_grouped(B, H, H_kv, N, d, torch.bfloat16, std, seed)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    g = torch.Generator(device="cpu").manual_seed(seed + 1)
+    do = torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    o, lse = binding.attention_forward(q, k, v, scale, causal, None)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = binding.fa_bwd_workspace_size(B, H, N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def launch():
+        st = binding.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, scale, causal, None,
+                            ws.data_ptr(), need, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"fa_bwd failed: {binding.fa_status_str(st)}")
+
+    m_step, m_kern, m_min = time_launches(launch, steps, 5)
+    flops = 2.5 * algorithmic_flops(B, H, N, d, causal)
+    return {"workload": f"long_context_bwd: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 "
+                        f"{'causal' if causal else 'non-causal'} (dQ, dK, dV)",
+            "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5), "kernel_ms_min": round(m_min, 5),
+            "flop_per_step": int(flops), "tflops": round(flops / (m_kern * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(index, heads):
     """The oracle as it stands on `heads` whole heads of the workload."""
     import numpy as np
@@ -376,6 +412,8 @@ def main(argv=None):
         # head size 256 at the long-context size (same FLOP as H = 32, d = 128)
         others["long_context_d256"] = time_grouped(dev, stream.cuda_stream, H=16, H_kv=16, d=256, seed=8,
                                                    name="long_context_d256")
+        # gradients at the long-context size
+        others["long_context_bwd"] = time_backward(dev, stream.cuda_stream)
         # one decode step against a long key/value cache (HBM-bound)
         others["decode"] = time_decode(dev, stream.cuda_stream)
 

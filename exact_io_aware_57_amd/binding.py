@@ -22,8 +22,8 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_NO_DEVICE = -4
 FA_ERR_LAUNCH = -5
 
-EXPORTED_SYMBOLS = ("fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32",
-                    "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
+                    "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,11 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
             fn.restype = i32
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp,
+                               ctypes.c_size_t, vp]
+        lib.fa_bwd.restype = i32
+        lib.fa_bwd_workspace_size.argtypes = [i32, i32, i32]
+        lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, ctypes.c_size_t, vp]
         lib.fa_decode.restype = i32
         lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -95,6 +100,52 @@ def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, seqlens, st
     """C fa_fwd_gqa_f32 with integer device pointers (k, v have H_kv heads)."""
     return load().fa_fwd_gqa_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
                                  float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, seqlens, workspace, workspace_size,
+           stream):
+    """C fa_bwd with integer device pointers."""
+    return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), int(B),
+                         int(H), int(H_kv), int(N), int(d), float(scale), int(bool(causal)), _ptr(seqlens),
+                         _ptr(workspace), int(workspace_size), _ptr(stream))
+
+
+def fa_bwd_workspace_size(B, H, N):
+    """Bytes of workspace fa_bwd needs (0 for invalid arguments)."""
+    return int(load().fa_bwd_workspace_size(int(B), int(H), int(N)))
+
+
+def attention_backward(q, k, v, o, lse, dout, scale, causal=False, seqlens=None, dq=None, dk=None, dv=None,
+                       workspace=None, stream=None):
+    """(dq, dk, dv) for torch bf16 device tensors q, o, dout [B, H, N, d], k, v
+    [B, H_kv, N, d] and the forward pass's float32 lse [B, H, N].  Outputs and
+    the workspace are allocated with torch when not given."""
+    import torch
+
+    if q.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError(f"need q [B, H, N, d] and k, v [B, H_kv, N, d], got {tuple(q.shape)}, {tuple(k.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != q.shape[:3]:
+        raise ValueError("o and dout must match q, lse must be [B, H, N]")
+    if not all(x.dtype == torch.bfloat16 for x in (q, k, v, o, dout)) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if not all(x.is_cuda and x.is_contiguous() for x in (q, k, v, o, dout, lse)):
+        raise ValueError("inputs must be contiguous device tensors")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_size(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, scale, causal,
+                None if seqlens is None else seqlens.data_ptr(), workspace.data_ptr(), workspace.numel(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, workspace, workspace_size,

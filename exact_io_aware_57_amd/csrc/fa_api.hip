@@ -90,9 +90,47 @@ size_t workspace_bytes(int B, int H, int Nq, int d, int S) {
   return rows * (size_t)S * (size_t)d * sizeof(float) + rows * (size_t)S * sizeof(float);
 }
 
+int bwd_npad(int N) {
+  const int pad = fa::bwd_row_pad();
+  return (N + pad - 1) / pad * pad;
+}
+
+size_t bwd_workspace_bytes(int B, int H, int N) { return 2 * (size_t)B * H * (size_t)bwd_npad(N) * sizeof(float); }
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_bwd_workspace_size(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return bwd_workspace_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal, const int32_t* seqlens,
+           void* workspace, size_t workspace_size, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * H * N * d > (uint64_t(1) << 40)) return FA_ERR_INVALID_ARG;
+  const long long tiles = ((long long)N + 127) / 128;
+  if ((long long)B * H * tiles > INT32_MAX || (long long)B * H * (N + 64) > INT32_MAX) return FA_ERR_INVALID_ARG;
+  if (workspace_size < bwd_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16))
+    return FA_ERR_MISALIGNED;
+  if (!aligned(lse, 4)) return FA_ERR_MISALIGNED;
+  if (seqlens && !aligned(seqlens, 4)) return FA_ERR_MISALIGNED;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  const int Npad = bwd_npad(N);
+  float* lse2 = reinterpret_cast<float*>(workspace);
+  float* delta = lse2 + (size_t)B * H * Npad;
+  fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, seqlens, lse2, delta, B, H, H_kv, N, Npad, d, scale,
+                  causal ? 1 : 0};
+  return fa::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
 
 size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits) {
   if (!decode_shape_ok(B, H, H_kv, Nq, Nk, d) || num_splits < 0) return 0;

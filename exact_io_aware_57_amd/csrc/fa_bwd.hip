@@ -1,0 +1,527 @@
+// Gradients of exact attention (dQ, dK, dV), bf16 in / bf16 out, for gfx950.
+//
+// The pages quote their speed-ups for training but print no backward
+// algorithm (FlashAttention (UR), "Experimental results"; FlashAttention-2 (HI),
+// "Performance and efficiency").  What is computed is the chain rule through
+// the forward definition, for a loss whose gradient with respect to O is dO:
+//     P = softmax(scale Q K^T) (row-wise, masked),  dV = P^T dO,  dP = dO V^T,
+//     dS = P o (dP - D),  D_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
+// As in the forward pass, the N x N matrices never reach HBM: P is recomputed
+// tile by tile from Q, K and the forward pass's row log-sum-exp, the same
+// recomputation that lets the forward pass keep no attention matrix
+// (FlashAttention (UR), "Tiling and block-based processing").
+//
+// Three kernels, no atomics, a fixed order of every sum (bitwise repeatable):
+//  1. bwd_rowdot_kernel: D_i = dO_i . O_i and lse2_i = LSE_i log2(e) per query
+//     row, into the caller's workspace (rows padded to a multiple of 64 per
+//     head, the padding set to lse2 = +inf, D = 0).
+//  2. bwd_dkdv_kernel: one workgroup per (batch, key/value head, 128 keys);
+//     each wave holds its 32 keys' K and V rows as matrix operands and the
+//     transposed accumulators dV^T, dK^T, and streams 64-query tiles of Q, dO,
+//     lse2 and D (every query head of the group in turn) through LDS:
+//         S = Q K^T, P = exp2(S scale log2e - lse2), dP = dO V^T,
+//         dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
+//     Lanes own keys and registers hold queries, so P and dS feed the next
+//     products straight from the accumulators, as P^T does in the forward
+//     kernels with the roles of queries and keys exchanged.
+//  3. bwd_dq_kernel: one workgroup per (batch, head, 128 queries); each wave
+//     holds its 32 queries' Q and dO rows and dQ^T, and streams 64-key tiles of
+//     K and V:  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
+//     dQ^T += K^T dS^T.
+// Computing dQ in its own pass recomputes S and dP once more (7 products per
+// score instead of 5) in exchange for no atomic accumulation of dQ across key
+// tiles.
+//
+// Q and dO (kernel 2) and K (kernel 3) are read from LDS both as rows (A
+// operand of S, dP) and transposed (A operand of dK^T, dV^T, dQ^T, via
+// ds_read_b64_tr_b16), so their 16-byte chunks are stored with one XOR
+// swizzle that keeps both access patterns free of bank conflicts.
+// All three kernels run one wave per SIMD and keep the accumulators in the
+// accumulation registers (this source is compiled without the VGPR-form
+// option).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBT = 64;         // rows of a streamed tile (queries in kernel 2, keys in kernel 3)
+constexpr int kRowsWG = 128;    // rows held per workgroup (4 waves x 32)
+
+// Swizzle for tiles read both as rows and transposed: chunk c of row r is stored
+// at c ^ swz(r).  Rows: 16 lanes read one chunk of 16 consecutive rows, which
+// land in 16 distinct 16-byte bank groups.  Transposed: 32 lanes read 64 bytes
+// of 4 consecutive rows 4a..4a+3, which land in 4 distinct 64-byte bank windows
+// (d = 128: bits 2-3 of the swizzle differ; d = 64, two rows per 256 bytes:
+// rows 4a and 4a+2 differ in bit 2).
+template <int D>
+__device__ __forceinline__ int bswz(int row) {
+  return D == 64 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = dO_i . O_i and lse2_i; 16 lanes per row (8 elements each at d = 128,
+// 4 at d = 64), 16 rows per workgroup.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p) {
+  constexpr int EPL = D / 16;   // elements per lane
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * 16 + (tid >> 4);   // padded row index
+  const int sub = tid & 15;
+  const long long bh = row / p.Npad;
+  const int i = (int)(row - bh * p.Npad);
+  if (bh >= (long long)p.B * p.H) return;
+  float acc = 0.0f;
+  float lse = -INFINITY;
+  if (i < p.N) {
+    const size_t off = ((size_t)bh * p.N + i) * D + sub * EPL;
+    const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + off;
+    const __bf16* g = reinterpret_cast<const __bf16*>(p.dout) + off;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    lse = p.lse[(size_t)bh * p.N + i];
+  }
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, 16);
+  if (sub == 0) {
+    p.delta[row] = acc;
+    // a row with no allowed key (LSE = -inf) gets P = exp2(s - inf) = 0
+    p.lse2[row] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared operand addressing for a 64-row tile stored with bswz.
+// ---------------------------------------------------------------------------
+template <int D>
+struct TileAddr {
+  using T = Tile<D, kBT>;
+  int row_base;   // A operand of k-step s, rows blk*32 + r32: XOR with 32 s
+  int tr_base0;   // transposed read of rows 16u + 4hi + {0..3} of a 32-row block: XOR with 64 cb
+  int tr_base1;   // the same for rows 16u + 8 + 4hi + {0..3}
+  __device__ __forceinline__ TileAddr(int lane) {
+    const int r32 = lane & 31, hi = lane >> 5;
+    const int x = bswz<D>(r32);
+    row_base = r32 * T::ROW + ((((x >> 1) << 1) | (hi ^ (x & 1))) << 4);
+    const int i16 = lane & 15, g16 = (lane >> 4) & 1;
+    const int vrow = 4 * hi + (i16 >> 2);
+    const int c0 = 2 * g16 + ((i16 & 3) >> 1);
+    tr_base0 = vrow * T::ROW + ((c0 ^ bswz<D>(vrow)) << 4) + (i16 & 1) * 8;
+    tr_base1 = (vrow + 8) * T::ROW + ((c0 ^ bswz<D>(vrow + 8)) << 4) + (i16 & 1) * 8;
+  }
+};
+
+// Transposing read pair of rows (blk*32 + 16u) + {4hi + 0..3, 8 + 4hi + 0..3},
+// columns of row block cb: the A operand X^T[col][row] of one product.
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr(const char* tile, int tb0, int tb1, int blk, int u, int cb) {
+  using T = Tile<D, kBT>;
+  const char* base = tile + (blk * 32 + 16 * u) * T::ROW;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (tb0 ^ (cb << 6))));
+  const s16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (tb1 ^ (cb << 6))));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 hi2 = __builtin_bit_cast(u32x2, hv);
+  const u32x4 a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(bf16x8, a4);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const char* tile, int rb, int blk, int s) {
+  using T = Tile<D, kBT>;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + blk * 32 * T::ROW + (rb ^ (s << 5))));
+}
+
+// Direct global->LDS load of one 64-row tile (rows clamped to [0, N-1]); wave
+// w fills rows of its NLD wave-loads, chunk (lane % CH) of each.
+template <int D>
+__device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char* dst, int wave, int lane) {
+  using T = Tile<D, kBT>;
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i) {
+    const int pos = (wave * T::NLD + i) * 64 + lane;
+    const int row = pos / T::CH;
+    const int cst = pos % T::CH;
+    const int r = min(r0 + row, N - 1);
+    load_to_lds16(src + (size_t)r * D + ((cst ^ bswz<D>(row)) << 3), dst + (wave * T::NLD + i) * 1024);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+  using T = Tile<D, kBT>;
+  constexpr int DC = T::DC, DB = T::DB;
+  constexpr int STAGE = 2 * T::MAT + 2 * kBT * 4;   // Q, dO, lse2[64], D[64]
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int nkt = (N + kRowsWG - 1) / kRowsWG;
+  const int total = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = total >> 3;
+  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
+  const int bg = lid / nkt;
+  const int kt = lid - bg * nkt;   // ascending: under a causal mask the first key tiles have the most queries
+  const int b = bg / p.Hkv;
+  const int g = bg - b * p.Hkv;
+  const int G = p.H / p.Hkv;
+
+  int L = N;
+  if (p.seqlens) {
+    const int x = p.seqlens[b];
+    L = x < 0 ? 0 : (x > N ? N : x);
+  }
+  const int k0 = kt * kRowsWG;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + r32;          // this lane's key
+  const bool wave_live = kw0 < L;     // keys at or past L get zero gradients
+
+  const size_t kvoff = ((size_t)b * p.Hkv + g) * (size_t)N * D;
+  // K, V rows of this lane's key as B operands: element 16 s + 8 hi + e
+  bf16x8 kf[DC], vf[DC];
+  {
+    const int kr = min(key, N - 1);
+    const u32x4* krow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.k) + kvoff + (size_t)kr * D);
+    const u32x4* vrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.v) + kvoff + (size_t)kr * D);
+#pragma unroll
+    for (int s = 0; s < DC; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, krow[2 * s + hi]);
+      vf[s] = __builtin_bit_cast(bf16x8, vrow[2 * s + hi]);
+    }
+  }
+
+  const int nqt = (N + kBT - 1) / kBT;
+  const int qstart = CAUSAL ? k0 / kBT : 0;
+  const int per_head = nqt - qstart;
+  const int n_it = L > k0 ? G * per_head : 0;   // no valid key in this workgroup: nothing to accumulate
+
+  auto issue_loads = [&](int it, char* base) __attribute__((always_inline)) {
+    const int hq = g * G + it / per_head;
+    const int q0 = (qstart + it % per_head) * kBT;
+    const size_t hoff = ((size_t)b * p.H + hq) * (size_t)N * D;
+    load_tile<D>(reinterpret_cast<const __bf16*>(p.q) + hoff, q0, N, base, wave, lane);
+    load_tile<D>(reinterpret_cast<const __bf16*>(p.dout) + hoff, q0, N, base + T::MAT, wave, lane);
+    if (wave < 2 && lane < 16) {   // 64 floats of lse2 (wave 0) or D (wave 1)
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + hq) * (size_t)p.Npad + q0;
+      load_to_lds16(src + lane * 4, base + 2 * T::MAT + wave * kBT * 4);
+    }
+  };
+
+  f32x16 dvacc[DB], dkacc[DB];
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) {
+    dvacc[cb] = f32x16{};
+    dkacc[cb] = f32x16{};
+  }
+  const float sc = p.scale * kLog2e;
+  const TileAddr<D> ad(lane);
+
+  auto tile = [&](const bool MASK, const char* st, int q0) __attribute__((always_inline)) {
+    const char* Qs = st;
+    const char* Gs = st + T::MAT;
+    const float* ls = reinterpret_cast<const float*>(st + 2 * T::MAT);
+    const float* ds = ls + kBT;
+    int rb = ad.row_base, tb0 = ad.tr_base0, tb1 = ad.tr_base1;
+    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DC; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Qs, rb, qb, s), kf[s], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < DC; ++s) {
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Gs, rb, qb, s), vf[s], pacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register r holds query q0 + 32 qb + 8 (r / 4) + 4 hi + r % 4
+      uint32_t pk[8], dk[8];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+        const int qo = qb * 32 + 8 * gq + 4 * hi;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + qo);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * gq + e], sc, -l4[e]));
+          if (MASK) {
+            const int q = q0 + qo + e;
+            const bool ok = q < N && key < L && (!CAUSAL || key <= q);
+            pr = ok ? pr : 0.0f;
+          }
+          pv[e] = pr;
+          dsv[e] = pr * (pacc[4 * gq + e] - d4[e]);
+        }
+        pk[2 * gq] = pack_bf16(pv[0], pv[1]);
+        pk[2 * gq + 1] = pack_bf16(pv[2], pv[3]);
+        dk[2 * gq] = pack_bf16(dsv[0], dsv[1]);
+        dk[2 * gq + 1] = pack_bf16(dsv[2], dsv[3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, 16 at a time:
+      // half u takes registers 8u..8u+7, queries 16u + 4hi + {0..3, 8..11}
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 bp = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
+        const u32x4 bs = {dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]};
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, tb0, tb1, qb, u, cb),
+                                                              __builtin_bit_cast(bf16x8, bp), dvacc[cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, tb0, tb1, qb, u, cb),
+                                                              __builtin_bit_cast(bf16x8, bs), dkacc[cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int it, const char* cur, char* next) __attribute__((always_inline)) {
+    if (it + 1 < n_it) issue_loads(it + 1, next);
+    const int q0 = (qstart + it % per_head) * kBT;
+    const bool active = wave_live && (!CAUSAL || q0 + kBT - 1 >= kw0);
+    if (active) {
+      const bool need_mask = (q0 + kBT > N) || (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
+      if (need_mask)
+        tile(true, cur, q0);
+      else
+        tile(false, cur, q0);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (n_it > 0) issue_loads(0, stage0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, stage0, stage1);
+    if (it + 1 < n_it) step(it + 1, stage1, stage0);
+  }
+
+  // dV^T, dK^T register r: column 32 cb + 8 (r / 4) + 4 hi + r % 4 of this lane's key
+  if (key < N) {
+    __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv) + kvoff + (size_t)key * D;
+    __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk) + kvoff + (size_t)key * D;
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int col = cb * 32 + 8 * gq + 4 * hi;
+        const u32x2 wv = {pack_bf16(dvacc[cb][4 * gq], dvacc[cb][4 * gq + 1]),
+                          pack_bf16(dvacc[cb][4 * gq + 2], dvacc[cb][4 * gq + 3])};
+        const u32x2 wk = {pack_bf16(dkacc[cb][4 * gq] * p.scale, dkacc[cb][4 * gq + 1] * p.scale),
+                          pack_bf16(dkacc[cb][4 * gq + 2] * p.scale, dkacc[cb][4 * gq + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(dvrow + col) = wv;
+        *reinterpret_cast<u32x2*>(dkrow + col) = wk;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  using T = Tile<D, kBT>;
+  constexpr int DC = T::DC, DB = T::DB;
+  constexpr int STAGE = 2 * T::MAT;   // K, V
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int ntiles = (N + kRowsWG - 1) / kRowsWG;
+  const int total = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = total >> 3;
+  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
+  const int bh = lid / ntiles;
+  int qt = lid - bh * ntiles;
+  if (CAUSAL) qt = ntiles - 1 - qt;   // heaviest first
+  const int b = bh / p.H;
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * (size_t)N * D;
+  const __bf16* __restrict__ Kh = reinterpret_cast<const __bf16*>(p.k) + kvoff;
+  const __bf16* __restrict__ Vh = reinterpret_cast<const __bf16*>(p.v) + kvoff;
+
+  int L = N;
+  if (p.seqlens) {
+    const int x = p.seqlens[b];
+    L = x < 0 ? 0 : (x > N ? N : x);
+  }
+  const int q0 = qt * kRowsWG;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + r32;
+  int kv_end = L;
+  if (CAUSAL) kv_end = min(kv_end, q0 + kRowsWG);
+  const int ntk = (kv_end + kBT - 1) / kBT;
+
+  bf16x8 qf[DC], gf[DC];
+  {
+    const int qr = min(qi, N - 1);
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.q) + hoff + (size_t)qr * D);
+    const u32x4* grow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.dout) + hoff + (size_t)qr * D);
+#pragma unroll
+    for (int s = 0; s < DC; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, qrow[2 * s + hi]);
+      gf[s] = __builtin_bit_cast(bf16x8, grow[2 * s + hi]);
+    }
+  }
+  const float lse2 = p.lse2[(size_t)bh * p.Npad + min(qi, p.Npad - 1)];
+  const float dsum = p.delta[(size_t)bh * p.Npad + min(qi, p.Npad - 1)];
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) dqacc[cb] = f32x16{};
+  const float sc = p.scale * kLog2e;
+  const TileAddr<D> ad(lane);
+
+  auto tile = [&](const bool MASK, const char* st, int k0) __attribute__((always_inline)) {
+    const char* Ks = st;
+    const char* Vs = st + T::MAT;
+    int rb = ad.row_base, tb0 = ad.tr_base0, tb1 = ad.tr_base1;
+    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DC; ++s) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Ks, rb, kb, s), qf[s], sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < DC; ++s) {
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Vs, rb, kb, s), gf[s], pacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register r holds key k0 + 32 kb + 8 (r / 4) + 4 hi + r % 4
+      uint32_t dk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * j + e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], sc, -lse2));
+          if (MASK) {
+            const int kk = k0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const bool ok = kk < L && (!CAUSAL || kk <= qi);
+            pr = ok ? pr : 0.0f;
+          }
+          dsv[e] = pr * (pacc[r] - dsum);
+        }
+        dk[j] = pack_bf16(dsv[0], dsv[1]);
+      }
+      // dQ^T += K^T dS^T over these 32 keys, 16 at a time
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 bs = {dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]};
+#pragma unroll
+        for (int cb = 0; cb < DB; ++cb) {
+          dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Ks, tb0, tb1, kb, u, cb),
+                                                              __builtin_bit_cast(bf16x8, bs), dqacc[cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  };
+
+  auto issue_loads = [&](int t, char* base) __attribute__((always_inline)) {
+    load_tile<D>(Kh, t * kBT, N, base, wave, lane);
+    load_tile<D>(Vh, t * kBT, N, base + T::MAT, wave, lane);
+  };
+
+  auto step = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
+    if (t + 1 < ntk) issue_loads(t + 1, next);
+    const int k0 = t * kBT;
+    const bool active = !CAUSAL || (k0 <= qw0 + 31);
+    if (active) {
+      const bool need_mask = (k0 + kBT > L) || (CAUSAL && k0 + kBT - 1 > qw0);
+      if (need_mask)
+        tile(true, cur, k0);
+      else
+        tile(false, cur, k0);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (ntk > 0) issue_loads(0, stage0);
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < ntk; t += 2) {
+    step(t, stage0, stage1);
+    if (t + 1 < ntk) step(t + 1, stage1, stage0);
+  }
+
+  if (qi < N) {
+    __bf16* orow = reinterpret_cast<__bf16*>(p.dq) + hoff + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int col = cb * 32 + 8 * gq + 4 * hi;
+        const u32x2 w = {pack_bf16(dqacc[cb][4 * gq] * p.scale, dqacc[cb][4 * gq + 1] * p.scale),
+                         pack_bf16(dqacc[cb][4 * gq + 2] * p.scale, dqacc[cb][4 * gq + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(orow + col) = w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
+  BwdParams arg = p;
+  void* args[] = {&arg};
+  const long long rows = (long long)p.B * p.H * p.Npad;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_rowdot_kernel<D>), dim3((unsigned)((rows + 15) / 16)),
+                                 dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  const unsigned nt = (unsigned)((p.N + kRowsWG - 1) / kRowsWG);
+  const void* kv = p.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, true>)
+                            : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, false>);
+  e = hipLaunchKernel(kv, dim3(nt * (unsigned)p.B * (unsigned)p.Hkv), dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess) return e;
+  const void* dq = p.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, true>)
+                            : reinterpret_cast<const void*>(&bwd_dq_kernel<D, false>);
+  return hipLaunchKernel(dq, dim3(nt * (unsigned)p.B * (unsigned)p.H), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+int bwd_row_pad() { return kBT; }
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  return p.d == 64 ? launch_all<64>(p, stream) : launch_all<128>(p, stream);
+}
+
+}  // namespace fa

@@ -47,6 +47,31 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16_d256(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// Backward pass.  lse2 and delta point into the caller's workspace: per query
+// row (rows of each head padded to Npad, a multiple of bwd_row_pad()) the
+// forward LSE times log2(e) and D = dO . O.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* seqlens;   // may be null
+  float* lse2;
+  float* delta;
+  int B, H, Hkv, N, Npad, d;
+  float scale;
+  int causal;
+};
+
+// Enqueues the row-dot kernel, the dK/dV kernel and the dQ kernel.
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+int bwd_row_pad();
 int decode_rows_per_block();   // query rows per split-kernel workgroup
 int decode_tile_keys();        // keys per tile of the split kernel
 

@@ -137,6 +137,40 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Bytes of workspace fa_decode needs for these arguments (0 for invalid ones). */
 size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits);
 
+/*
+ * Backward pass: dQ, dK, dV for a loss whose gradient with respect to the
+ * forward output O is dout.  The pages print no backward algorithm; this is the
+ * chain rule through the forward definition:
+ *   P = softmax(scale Q K^T) (masked), dV = P^T dO, dP = dO V^T,
+ *   dS = P o (dP - D) with D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q,
+ * with P recomputed tile by tile from Q, K and the forward LSE, as the forward
+ * pass computes it without storing the attention matrix (FlashAttention (UR),
+ * "Tiling and block-based processing").
+ *   q, o, dout : [B, H, N, d] bf16 (o and lse are the forward pass's outputs)
+ *   k, v       : [B, H_kv, N, d] bf16 (H_kv divides H, grouped as fa_fwd_gqa)
+ *   lse        : float [B, H, N], the forward pass's row log-sum-exp (required)
+ *   dq         : [B, H, N, d] bf16 output
+ *   dk, dv     : [B, H_kv, N, d] bf16 outputs; with grouped heads, the sum over
+ *                the query heads that share the key/value head
+ *   d          : 64 or 128
+ *   scale, causal, seqlens : as for the forward call that produced o and lse
+ *   workspace, workspace_size : caller-owned device memory of at least
+ *                fa_bwd_workspace_size(B, H, N) bytes (16-byte aligned) for the
+ *                per-row D and LSE log2(e); its contents on entry do not matter
+ * Arithmetic: bf16 products on matrix cores with float32 accumulation; P and dS
+ * are rounded to bf16 as operands of the gradient products; every sum has a
+ * fixed order (no atomics), so results are bitwise repeatable.  Keys at or past
+ * a batch's padding length get zero dK, dV.  Enqueues three kernels on stream;
+ * returns FA_OK or a negative fa_status (FA_ERR_INVALID_ARG also for a
+ * workspace smaller than required); nothing is enqueued on error.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+           const int32_t* seqlens, void* workspace, size_t workspace_size, void* stream);
+
+/* Bytes of workspace fa_bwd needs (0 for invalid arguments). */
+size_t fa_bwd_workspace_size(int B, int H, int N);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

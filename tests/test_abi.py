@@ -30,8 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_gqa",
-                                    "fa_fwd_gqa_f32", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
+                                    "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -170,3 +170,41 @@ def test_decode_arguments_are_checked_on_the_host(lib):
     assert call_dec(d=256) == E.FA_ERR_UNSUPPORTED
     assert call_dec(workspace=FAKE + 4) == E.FA_ERR_MISALIGNED
     assert call_dec(q=FAKE + 8) == E.FA_ERR_MISALIGNED
+
+
+BWD = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=2, H=8, H_kv=2, N=1000,
+           d=128, scale=0.1, causal=1, seqlens=None, workspace=FAKE, workspace_size=1 << 30, stream=None)
+
+
+def call_bwd(**over):
+    a = dict(BWD)
+    a.update(over)
+    return binding.fa_bwd(*(a[n] for n in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "B", "H", "H_kv", "N",
+                                            "d", "scale", "causal", "seqlens", "workspace", "workspace_size",
+                                            "stream")))
+
+
+def test_bwd_workspace_size(lib):
+    f = binding.fa_bwd_workspace_size
+    # two floats per query row, rows of each head padded to a multiple of 64
+    assert f(2, 8, 1000) == 2 * 2 * 8 * 1024 * 4
+    assert f(1, 1, 64) == 2 * 64 * 4
+    assert f(1, 1, 1) == 2 * 64 * 4
+    assert f(0, 1, 1) == 0 and f(1, 0, 1) == 0 and f(1, 1, 0) == 0
+
+
+def test_bwd_arguments_are_checked_on_the_host(lib):
+    E = binding
+    for name in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "workspace"):
+        assert call_bwd(**{name: None}) == E.FA_ERR_INVALID_ARG, name
+    for over in (dict(B=0), dict(N=0), dict(H=-1), dict(H_kv=3), dict(H_kv=16), dict(scale=0.0),
+                 dict(scale=float("nan")), dict(workspace_size=16)):
+        assert call_bwd(**over) == E.FA_ERR_INVALID_ARG, over
+    for d in (32, 96, 256):
+        assert call_bwd(d=d) == E.FA_ERR_UNSUPPORTED, d
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv", "workspace"):
+        assert call_bwd(**{name: FAKE + 8}) == E.FA_ERR_MISALIGNED, name
+    assert call_bwd(lse=FAKE + 2) == E.FA_ERR_MISALIGNED
+    assert call_bwd(seqlens=FAKE + 1) == E.FA_ERR_MISALIGNED
+    # valid arguments reach the device check (no GPU here)
+    assert call_bwd() == E.FA_ERR_NO_DEVICE

@@ -128,6 +128,31 @@ def random_decode(B, H, H_kv, Nq, Nk, d, dtype=torch.bfloat16, std=1.0, seed=0, 
     return out[0], out[1], out[2], seqlens
 
 
+def random_qkv_fp8(B, H, H_kv, N, d, std=1.0, seed=0, len_range=None):
+    """FP8 (e4m3) inputs with per-tensor scales: (q8, k8, v8, descale, seqlens).
+
+    Q [B, H, N, d] and K, V [B, H_kv, N, d] are drawn like ``random_qkv_grouped``
+    in float32, each tensor is divided by descale = max|x| / 448 so that its
+    largest magnitude is the format's largest finite value, and rounded to e4m3
+    by torch (round to nearest even).  q8, k8, v8 are uint8 CPU tensors of the
+    codes; descale is a tuple of three floats, the tensor a code array stands
+    for being descale * value(code)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    codes, descale = [], []
+    for shape in ((B, H, N, d), (B, H_kv, N, d), (B, H_kv, N, d)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x = x * std
+        s = float(x.abs().max()) / 448.0
+        s = s if s > 0 else 1.0
+        codes.append((x / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+        descale.append(s)
+    seqlens = None
+    if len_range is not None:
+        seqlens = random_seqlens(B, len_range[0], len_range[1], g)
+    return codes[0], codes[1], codes[2], tuple(descale), seqlens
+
+
 def make_inputs(index, seed=None):
     """Inputs of a numbered workload: dict(q, k, v, seqlens, scale, causal, wl).
 

@@ -20,7 +20,8 @@ attention : the definition in numpy float64 (``attention``, ``attention_rows``,
             ``softmax_matrix``, ``kv_head`` for grouped / multi-query
             attention, ``attention_decode`` for a few queries against a key
             cache, ``merge_partials`` for combining results over disjoint key
-            sets).  Every function is pinned by tests/test_oracle.py.
+            sets, ``e4m3_decode`` and ``attention_fp8`` for FP8 inputs with
+            per-tensor scales).  Every function is pinned by tests/test_oracle.py.
 backward  : ``attention_backward``, the gradients dQ, dK, dV of the definition by
             the chain rule (the pages give no backward algorithm).
 brute     : the same definition as scalar Python loops with ``math.exp`` and
@@ -28,7 +29,8 @@ brute     : the same definition as scalar Python loops with ``math.exp`` and
             only to pin ``attention`` on tiny inputs.
 """
 from .attention import (  # noqa: F401
-    allowed_mask, attention, attention_decode, attention_rows, decode_allowed, kv_head, merge_partials, softmax_matrix,
+    allowed_mask, attention, attention_decode, attention_fp8, attention_rows, decode_allowed, e4m3_decode, kv_head,
+    merge_partials, softmax_matrix,
 )
 from .backward import attention_backward  # noqa: F401
 from .brute import attention_brute  # noqa: F401

@@ -27,7 +27,7 @@ LSE_i = log(sum_{j allowed} exp(s_ij)), computed stably as m_i + log(l_i).
 import numpy as np
 
 __all__ = ["allowed_mask", "softmax_matrix", "attention_rows", "attention", "kv_head", "decode_allowed", "attention_decode",
-           "merge_partials"]
+           "merge_partials", "e4m3_decode", "attention_fp8"]
 
 
 def _f64(x):
@@ -206,3 +206,38 @@ def merge_partials(o_parts, lse_parts):
     lse = np.where(finite, mm + np.log(np.where(finite, tot, 1.0)), -np.inf)
     o = np.einsum("...s,...sd->...d", np.divide(w, np.where(finite, tot, 1.0)[..., None]), o_parts)
     return o, lse
+
+
+# ---------------------------------------------------------------------------------
+# FP8 inputs.
+# ---------------------------------------------------------------------------------
+def e4m3_decode(codes):
+    """Values of 8-bit floats in the OCP e4m3 ("E4M3FN") format, float64.
+
+    FlashAttention (UR), section "FlashAttention-3 (2024)", names FP8 support
+    without a format; the reading used here is the 8-bit format with 1 sign bit,
+    4 exponent bits (bias 7) and 3 mantissa bits, no infinities, and NaN only
+    for the all-ones exponent-and-mantissa code (0x7F, 0xFF):
+      exponent field 0:    (-1)^s * (m / 8) * 2^-6         (subnormal, and zero)
+      exponent field e>0:  (-1)^s * (1 + m / 8) * 2^(e - 7)
+    so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def attention_fp8(q8, k8, v8, scale, descale, causal=False, seqlens=None):
+    """O and LSE (float64) of attention over FP8 inputs with per-tensor scales.
+
+    q8, k8, v8 hold e4m3 codes (uint8, shapes as for ``attention``); the tensors
+    they stand for are descale[0] * decode(q8), descale[1] * decode(k8) and
+    descale[2] * decode(v8).  The result is the definition applied to those
+    tensors: the exact answer for the quantised inputs.
+    """
+    sq, sk, sv = (float(x) for x in descale)
+    return attention(sq * e4m3_decode(q8), sk * e4m3_decode(k8), sv * e4m3_decode(v8), scale, causal, seqlens)

@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s (bf16, 1 GPU) and % of MFMA bf16 dense peak"
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS                # 5033.2 (dense fp8 matrix rate, twice bf16)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_io_aware_57_amd/csrc/fa_fwd_bf16.hip", "exact_io_aware_57_amd/csrc/fa_device.h",
                   "exact_io_aware_57_amd/csrc/fa_internal.h"]
@@ -264,6 +265,35 @@ def time_backward(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal
             "frac_of_bf16_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def time_fp8(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal=True, std=0.5, seed=10, steps=20):
+    """Kernel time of fa_fwd_fp8 (e4m3 inputs, per-tensor scales) on seeded
+    inputs; priced against the dense fp8 matrix peak."""
+    import torch
+
+    from exact_io_aware_57_amd import binding
+    from exact_io_aware_57_amd.inputs import random_qkv_fp8
+
+    q8, k8, v8, ds, _ = random_qkv_fp8(B, H, H_kv, N, d, std, seed)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+    def launch():
+        st = binding.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv,
+                                N, d, scale, ds[0], ds[1], ds[2], causal, None, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd_fp8 failed: {binding.fa_status_str(st)}")
+
+    m_step, m_kern, m_min = time_launches(launch, steps, 10)
+    flops = algorithmic_flops(B, H, N, d, causal)
+    return {"workload": f"long_context_fp8: B={B} H={H} H_kv={H_kv} N={N} d={d} e4m3 in, bf16 out "
+                        f"{'causal' if causal else 'non-causal'}",
+            "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5), "kernel_ms_min": round(m_min, 5),
+            "tflops": round(flops / (m_kern * 1e-3) / 1e12, 2),
+            "frac_of_fp8_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+
+
 def cpu_baseline(index, heads):
     """The oracle as it stands on `heads` whole heads of the workload."""
     import numpy as np
@@ -412,6 +442,8 @@ def main(argv=None):
         # head size 256 at the long-context size (same FLOP as H = 32, d = 128)
         others["long_context_d256"] = time_grouped(dev, stream.cuda_stream, H=16, H_kv=16, d=256, seed=8,
                                                    name="long_context_d256")
+        # FP8 inputs at the long-context size
+        others["long_context_fp8"] = time_fp8(dev, stream.cuda_stream)
         # gradients at the long-context size
         others["long_context_bwd"] = time_backward(dev, stream.cuda_stream)
         # one decode step against a long key/value cache (HBM-bound)

@@ -23,7 +23,7 @@ FA_ERR_NO_DEVICE = -4
 FA_ERR_LAUNCH = -5
 
 EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
-                    "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
+                    "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,8 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
             fn.restype = i32
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, f32, i32, vp, vp]
+        lib.fa_fwd_fp8.restype = i32
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp,
                                ctypes.c_size_t, vp]
         lib.fa_bwd.restype = i32
@@ -100,6 +102,38 @@ def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, seqlens, st
     """C fa_fwd_gqa_f32 with integer device pointers (k, v have H_kv heads)."""
     return load().fa_fwd_gqa_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
                                  float(scale), int(bool(causal)), _ptr(seqlens), _ptr(stream))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, d, scale, q_descale, k_descale, v_descale, causal, seqlens, stream):
+    """C fa_fwd_fp8 with integer device pointers."""
+    return load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(N), int(d),
+                             float(scale), float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+                             _ptr(seqlens), _ptr(stream))
+
+
+def attention_forward_fp8(q8, k8, v8, descale, scale, causal=False, seqlens=None, out=None, lse=None, stream=None,
+                          want_lse=True):
+    """O (bf16) and LSE for uint8 device tensors of e4m3 codes q8 [B, H, N, d],
+    k8, v8 [B, H_kv, N, d] standing for descale[i] * value(code)."""
+    import torch
+
+    if q8.dim() != 4 or k8.shape != v8.shape or k8.shape[0] != q8.shape[0] or k8.shape[2:] != q8.shape[2:]:
+        raise ValueError(f"need q8 [B, H, N, d] and k8, v8 [B, H_kv, N, d], got {tuple(q8.shape)}, {tuple(k8.shape)}")
+    if not all(x.dtype == torch.uint8 and x.is_cuda and x.is_contiguous() for x in (q8, k8, v8)):
+        raise ValueError("q8, k8, v8 must be contiguous uint8 device tensors")
+    B, H, N, d = q8.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), None if lse is None else lse.data_ptr(),
+                    B, H, k8.shape[1], N, d, scale, descale[0], descale[1], descale[2], causal,
+                    None if seqlens is None else seqlens.data_ptr(), stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return out, lse
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, seqlens, workspace, workspace_size,

@@ -194,6 +194,20 @@ int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, flo
   return run(p, stream, false);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+               int causal, const int32_t* seqlens, void* stream) {
+  fa::FwdParams p{q, k, v, o, lse, seqlens, B, H, N, d, H_kv, scale, causal ? 1 : 0, q_descale, k_descale, v_descale};
+  int st = validate(p);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  for (float s : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(s) || !(s > 0.0f)) return FA_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != FA_OK) return st;
+  return fa::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

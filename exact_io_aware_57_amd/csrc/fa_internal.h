@@ -19,6 +19,8 @@ struct FwdParams {
   int Hkv;                  // key/value heads; divides H (H: plain multi-head)
   float scale;
   int causal;
+  // FP8 inputs only: the tensors are descale * value(code)
+  float descale_q = 1.0f, descale_k = 1.0f, descale_v = 1.0f;
 };
 
 // One decode problem (few queries against a key/value cache), already
@@ -45,6 +47,7 @@ struct DecodeParams {
 // the merge kernel.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_bf16_d256(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

@@ -138,6 +138,25 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits);
 
 /*
+ * FP8 forward pass: Q, K, V as e4m3 codes with one scale per tensor.
+ *   q        : uint8 [B, H, N, d] e4m3 codes (OCP 8-bit float: 1 sign, 4
+ *              exponent bits with bias 7, 3 mantissa bits, max 448, NaN only
+ *              for 0x7F / 0xFF); the query tensor is q_descale * value(q)
+ *   k, v     : uint8 [B, H_kv, N, d] e4m3 codes, scaled by k_descale, v_descale
+ *   o        : __hip_bfloat16 [B, H, N, d] output;  lse : float [B, H, N] or NULL
+ *   d        : 64 or 128;  descales: finite and > 0;  other arguments as fa_fwd_gqa
+ * FlashAttention (UR), section "FlashAttention-3 (2024)", names FP8 support.
+ * Arithmetic: S = Q K^T on 8-bit matrix cores with float32 accumulation; the
+ * softmax in float32 with the exact running row max; P scaled by 2^8 and
+ * rounded to e4m3 (relative error <= 2^-4) for O += P V on 8-bit matrix cores;
+ * the row sum l adds the float32 P.  Returns FA_OK or a negative fa_status;
+ * nothing is enqueued on error.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, float q_descale, float k_descale, float v_descale,
+               int causal, const int32_t* seqlens, void* stream);
+
+/*
  * Backward pass: dQ, dK, dV for a loss whose gradient with respect to the
  * forward output O is dout.  The pages print no backward algorithm; this is the
  * chain rule through the forward definition:

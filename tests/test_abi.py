@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
-                                    "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
+                                    "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -208,3 +208,29 @@ def test_bwd_arguments_are_checked_on_the_host(lib):
     assert call_bwd(seqlens=FAKE + 1) == E.FA_ERR_MISALIGNED
     # valid arguments reach the device check (no GPU here)
     assert call_bwd() == E.FA_ERR_NO_DEVICE
+
+
+F8 = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, H=8, H_kv=2, N=1000, d=128, scale=0.1, sq=0.01, sk=0.02,
+          sv=0.03, causal=1, seqlens=None, stream=None)
+
+
+def call_fp8(**over):
+    a = dict(F8)
+    a.update(over)
+    return binding.fa_fwd_fp8(*(a[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "H_kv", "N", "d", "scale", "sq", "sk",
+                                                "sv", "causal", "seqlens", "stream")))
+
+
+def test_fp8_arguments_are_checked_on_the_host(lib):
+    E = binding
+    for name in ("q", "k", "v", "o"):
+        assert call_fp8(**{name: None}) == E.FA_ERR_INVALID_ARG, name
+    for over in (dict(B=0), dict(N=0), dict(H_kv=3), dict(scale=0.0), dict(sq=0.0), dict(sk=-1.0),
+                 dict(sv=float("inf")), dict(sq=float("nan"))):
+        assert call_fp8(**over) == E.FA_ERR_INVALID_ARG, over
+    for d in (32, 96, 256):
+        assert call_fp8(d=d) == E.FA_ERR_UNSUPPORTED, d
+    for name in ("q", "k", "v", "o"):
+        assert call_fp8(**{name: FAKE + 8}) == E.FA_ERR_MISALIGNED, name
+    assert call_fp8(lse=FAKE + 2) == E.FA_ERR_MISALIGNED
+    assert call_fp8() == E.FA_ERR_NO_DEVICE

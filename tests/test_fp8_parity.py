@@ -1,0 +1,136 @@
+"""GPU parity of the FP8 forward pass (fa_fwd_fp8) against the float64 oracle.
+
+The oracle is ``oracle.attention_fp8``: exact attention over the tensors the
+e4m3 codes stand for (descale * value).  Tolerance, derived from the kernel's
+arithmetic: the products of e4m3 values are exact and the 8-bit matrix
+instruction accumulates them with a relative error below 2^-12 of the sum of
+absolute terms (measured at about 2^-15), so a score is off by at most
+e_s = 2^-12 scale sum_c |q_c| |k_c| and its weight by a factor exp(e_s); P * 2^8
+is rounded to e4m3 with a relative error of at most 2^-4 (values under 2^-14
+keep fewer bits but add at most 2^-18 per key); the row sum adds the unrounded
+P in float32; the output is rounded to bf16 (2^-9).  Hence, per row i and column c,
+    |O err| <= (2^-4 + max_j expm1(e_s,ij) + 2^-12) sum_j w_ij |V_jc|
+               + N 2^-18 max|V| + 2^-9 |O|
+    |LSE err| <= max_j e_s,ij + 2^-20 |LSE|
+with w the exact softmax weights, and the tests require the error within twice
+that bound (plus 1e-6); the normwise relative error of O must stay within 2^-4.
+A CPU emulation of the kernel's rounding lands at 0.1-0.35 of the O bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_57_amd import binding
+from exact_io_aware_57_amd.inputs import random_qkv_fp8
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def decoded(q8, k8, v8, descale):
+    return tuple(oracle.e4m3_decode(c.numpy()) * s for c, s in zip((q8, k8, v8), descale))
+
+
+def row_bounds(qn, kn, vn, scale, causal, seqlens, b, h, rows):
+    """O and LSE error bounds of the listed rows of head (b, h)."""
+    N = kn.shape[2]
+    g = oracle.kv_head(h, qn.shape[1], kn.shape[1])
+    L = N if seqlens is None else min(max(int(seqlens[b]), 0), N)
+    w, _, _ = oracle.softmax_matrix(qn[b, h, rows], kn[b, g], scale, rows, L, causal)
+    allowed = oracle.allowed_mask(rows, N, L, causal)
+    es = 2.0 ** -12 * scale * (np.abs(qn[b, h, rows]) @ np.abs(kn[b, g]).T)
+    es = np.where(allowed, es, 0.0).max(axis=1)
+    bo = (2.0 ** -4 + np.expm1(es)[:, None] + 2.0 ** -12) * (w @ np.abs(vn[b, g])) + N * 2.0 ** -18 * np.abs(vn[b, g]).max()
+    return bo, es
+
+
+def gpu_fp8(q8, k8, v8, descale, scale, causal, seqlens):
+    sd = None if seqlens is None else seqlens.to(DEV)
+    o, lse = binding.attention_forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), descale, scale, causal, sd)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(q8, k8, v8, descale, scale, causal, seqlens, tag, heads=None, rows=None):
+    B, H, N, d = q8.shape
+    say(f"[fp8] {tag}: q {tuple(q8.shape)} k {tuple(k8.shape)} causal={causal} descale={descale} "
+        f"seqlens={None if seqlens is None else seqlens.tolist()}")
+    o, lse = gpu_fp8(q8, k8, v8, descale, scale, causal, seqlens)
+    og, lg = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.isfinite(og).all()
+    qn, kn, vn = decoded(q8, k8, v8, descale)
+    sl = None if seqlens is None else seqlens.numpy()
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    rows = np.arange(N) if rows is None else rows
+    worst, worst_l, err2, ref2 = 0.0, 0.0, 0.0, 0.0
+    for b, h in heads:
+        o_ref, lse_ref = oracle.attention_rows(qn, kn, vn, scale, causal, sl, b, h, rows)
+        bo, es = row_bounds(qn, kn, vn, scale, causal, sl, b, h, rows)
+        e = np.abs(og[b, h, rows] - o_ref)
+        worst = max(worst, (e / (2.0 * (bo + 2.0 ** -9 * np.abs(o_ref)) + 1e-6)).max())
+        err2 += (e ** 2).sum()
+        ref2 += (o_ref ** 2).sum()
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lg[b, h, rows]), fin)
+        assert np.all(og[b, h, rows][~fin] == 0.0)
+        if fin.any():
+            el = np.abs(lg[b, h, rows][fin] - lse_ref[fin])
+            worst_l = max(worst_l, (el / (2.0 * (es[fin] + 2.0 ** -20 * np.abs(lse_ref[fin])) + 1e-6)).max())
+    rel = math.sqrt(err2 / max(ref2, 1e-300))
+    say(f"[fp8] {tag}: O worst err/bound {worst:.3f} normwise rel {rel:.3e}; LSE worst err/bound {worst_l:.3f}")
+    assert worst <= 1.0 and worst_l <= 1.0
+    assert rel <= 2.0 ** -4
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (8, 2), (6, 1)])
+def test_fp8_parity(H, H_kv, d, causal):
+    for n, lens in [(200, None), (333, (1, 333))]:
+        q8, k8, v8, ds, sl = random_qkv_fp8(2, H, H_kv, n, d, 1.0, 60 + H_kv + n + d, lens)
+        check(q8, k8, v8, ds, 1.0 / math.sqrt(d), causal, sl, f"H={H}/{H_kv} n={n} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ragged_lengths(d, causal):
+    for n in [1, 2, 31, 33, 63, 64, 65, 127, 128, 129, 255, 257, 500]:
+        q8, k8, v8, ds, _ = random_qkv_fp8(1, 2, 2, n, d, 1.0, 4000 + n)
+        check(q8, k8, v8, ds, 1.0 / math.sqrt(d), causal, None, f"ragged n={n} d={d}")
+
+
+def test_fp8_padding_lengths():
+    n = 300
+    q8, k8, v8, ds, _ = random_qkv_fp8(6, 2, 1, n, 128, 1.0, 18)
+    sl = torch.tensor([0, 1, 63, 64, 65, n], dtype=torch.int32)
+    for causal in (False, True):
+        check(q8, k8, v8, ds, 0.0884, causal, sl, f"padding causal={causal}")
+
+
+def test_fp8_descales_and_peaked_scores():
+    """Large descales (scores of tens, nearly one-hot rows) and small ones."""
+    q8, k8, v8, _, _ = random_qkv_fp8(2, 4, 2, 257, 64, 1.0, 19)
+    for ds in [(0.01, 0.01, 0.01), (0.02, 0.03, 2.0), (1.0 / 448, 1.0 / 448, 1.0)]:
+        for causal in (False, True):
+            check(q8, k8, v8, ds, 0.125, causal, None, f"descale {ds}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_large_grid(causal):
+    """Many workgroups per head (sampled rows, every row checked for finiteness),
+    and bitwise repeatable."""
+    q8, k8, v8, ds, _ = random_qkv_fp8(1, 16, 4, 4096, 128, 1.0, 23 + causal)
+    rng = np.random.default_rng(causal)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4094, 4095], rng.integers(0, 4096, size=40)]))
+    o1, l1 = check(q8, k8, v8, ds, 0.0884, causal, None, "large grid", heads=[(0, 0), (0, 7), (0, 15)], rows=rows)
+    o2, l2 = gpu_fp8(q8, k8, v8, ds, 0.0884, causal, None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

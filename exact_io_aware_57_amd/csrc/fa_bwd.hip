@@ -135,6 +135,26 @@ __device__ __forceinline__ bf16x8 read_row(const char* tile, int rb, int blk, in
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + blk * 32 * T::ROW + (rb ^ (s << 5))));
 }
 
+// A sequence of N products in order, product i taking the A operand rd(i):
+// each operand is read from LDS kAhead products before its product, so the
+// reads are in flight under the matrix work (a scheduling fence after every
+// product keeps the compiler from hoisting a whole tile's reads).
+constexpr int kAhead = 4;
+
+template <int N, typename RD, typename MF>
+__device__ __forceinline__ void products(RD rd, MF mf) {
+  bf16x8 ring[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead && i < N; ++i) ring[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % kAhead];
+    if (i + kAhead < N) ring[i % kAhead] = rd(i + kAhead);
+    mf(i, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Direct global->LDS load of one 64-row tile (rows clamped to [0, N-1]); wave
 // w fills rows of its NLD wave-loads, chunk (lane % CH) of each.
 template <int D>
@@ -240,16 +260,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb) {
       // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DC; ++s) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Qs, rb, qb, s), kf[s], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int s = 0; s < DC; ++s) {
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Gs, rb, qb, s), vf[s], pacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      products<2 * DC>(
+          [&](int i) __attribute__((always_inline)) { return i < DC ? read_row<D>(Qs, rb, qb, i) : read_row<D>(Gs, rb, qb, i - DC); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            if (i < DC)
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i], sacc, 0, 0, 0);
+            else
+              pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i - DC], pacc, 0, 0, 0);
+          });
       // register r holds query q0 + 32 qb + 8 (r / 4) + 4 hi + r % 4
       uint32_t pk[8], dk[8];
 #pragma unroll
@@ -277,20 +295,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries, 16 at a time:
       // half u takes registers 8u..8u+7, queries 16u + 4hi + {0..3, 8..11}
+      // product i: half u = i / (2 DB), column block cb = (i / 2) % DB, dV (even i) or dK (odd i)
+      bf16x8 bp[2], bs[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const u32x4 bp = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
-        const u32x4 bs = {dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]};
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb) {
-          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Gs, tb0, tb1, qb, u, cb),
-                                                              __builtin_bit_cast(bf16x8, bp), dvacc[cb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Qs, tb0, tb1, qb, u, cb),
-                                                              __builtin_bit_cast(bf16x8, bs), dkacc[cb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        bp[u] = __builtin_bit_cast(bf16x8, u32x4{pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]});
+        bs[u] = __builtin_bit_cast(bf16x8, u32x4{dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]});
       }
+      products<4 * DB>(
+          [&](int i) __attribute__((always_inline)) {
+            return read_tr<D>((i & 1) ? Qs : Gs, tb0, tb1, qb, i / (2 * DB), (i / 2) % DB);
+          },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            const int u = i / (2 * DB), cb = (i / 2) % DB;
+            if (i & 1)
+              dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs[u], dkacc[cb], 0, 0, 0);
+            else
+              dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp[u], dvacc[cb], 0, 0, 0);
+          });
     }
   };
 
@@ -412,16 +434,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DC; ++s) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Ks, rb, kb, s), qf[s], sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int s = 0; s < DC; ++s) {
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(Vs, rb, kb, s), gf[s], pacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      products<2 * DC>(
+          [&](int i) __attribute__((always_inline)) { return i < DC ? read_row<D>(Ks, rb, kb, i) : read_row<D>(Vs, rb, kb, i - DC); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            if (i < DC)
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i], sacc, 0, 0, 0);
+            else
+              pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[i - DC], pacc, 0, 0, 0);
+          });
       // register r holds key k0 + 32 kb + 8 (r / 4) + 4 hi + r % 4
       uint32_t dk[8];
 #pragma unroll
@@ -441,16 +461,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         dk[j] = pack_bf16(dsv[0], dsv[1]);
       }
       // dQ^T += K^T dS^T over these 32 keys, 16 at a time
+      bf16x8 bs[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 bs = {dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]};
-#pragma unroll
-        for (int cb = 0; cb < DB; ++cb) {
-          dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(Ks, tb0, tb1, kb, u, cb),
-                                                              __builtin_bit_cast(bf16x8, bs), dqacc[cb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int u = 0; u < 2; ++u)
+        bs[u] = __builtin_bit_cast(bf16x8, u32x4{dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]});
+      products<2 * DB>(
+          [&](int i) __attribute__((always_inline)) { return read_tr<D>(Ks, tb0, tb1, kb, i / DB, i % DB); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            dqacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs[i / DB], dqacc[i % DB], 0, 0, 0);
+          });
     }
   };
 

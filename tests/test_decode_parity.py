@@ -195,3 +195,11 @@ def test_decode_rejects_small_workspace_on_device():
     ws = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
     with pytest.raises(binding.FaError):
         binding.decode_forward(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, False, None, workspace=ws)
+
+
+def test_decode_bench_configuration():
+    """The configuration bench.py times: B = 8, H = 32, H_kv = 8, one new query
+    per head against a full cache of 32768 positions, d = 128, causal, std 0.5;
+    every output row against the oracle."""
+    q, k, v, _ = random_decode(8, 32, 8, 1, 32768, 128, std=0.5, seed=7)
+    check(q, k, v, float(np.float32(1.0 / np.sqrt(128.0))), True, None, "bench configuration")

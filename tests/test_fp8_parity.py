@@ -134,3 +134,13 @@ def test_fp8_large_grid(causal):
     o1, l1 = check(q8, k8, v8, ds, 0.0884, causal, None, "large grid", heads=[(0, 0), (0, 7), (0, 15)], rows=rows)
     o2, l2 = gpu_fp8(q8, k8, v8, ds, 0.0884, causal, None)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_long_context_full_size():
+    """The configuration bench.py times (B = 1, H = 32, N = 16384, d = 128,
+    causal, std 0.5): sampled rows of three heads within the derived bound."""
+    q8, k8, v8, ds, _ = random_qkv_fp8(1, 32, 32, 16384, 128, 0.5, 10)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 8191, 16382, 16383], rng.integers(0, 16384, size=30)]))
+    check(q8, k8, v8, ds, float(np.float32(1.0 / math.sqrt(128.0))), True, None, "long context",
+          heads=[(0, 0), (0, 17), (0, 31)], rows=rows)

@@ -186,6 +186,14 @@ def test_head_size_256_large_grid(causal):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_head_size_256_long_context_full_size():
+    """The configuration bench.py times for head size 256 (B = 1, H = 16,
+    N = 16384, causal, std 0.5): sampled rows of three heads."""
+    q, k, v, _ = random_qkv_grouped(1, 16, 16, 16384, 256, torch.bfloat16, 0.5, 8)
+    check_sampled_rows(q, k, v, 1.0 / 16.0, True, None, [(0, 0), (0, 9), (0, 15)], "d=256 long context", n_rows=30,
+                       seed=3)
+
+
 def test_grouped_query_equals_repeated_heads():
     # the kernel's grouped path against its own plain path on repeated K/V: bitwise equal
     q, k, v, _ = random_qkv_grouped(2, 8, 2, 257, 128, torch.bfloat16, 1.0, seed=9)

@@ -70,12 +70,28 @@ def compulsory_bytes(B, H, N, d, elt_bytes):
     return 4 * B * H * N * d * elt_bytes + 4 * B * H * N
 
 
-def kernel_source_hash():
+def source_hash(paths):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in paths:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash():
+    return source_hash(KERNEL_SOURCES)
+
+
+# every kernel source, for the summary of all kernels' traffic
+TRAFFIC_ALL_SOURCES = sorted(os.path.join("exact_io_aware_57_amd", "csrc", f)
+                             for f in os.listdir(os.path.join(ROOT, "exact_io_aware_57_amd", "csrc"))
+                             if f.endswith((".hip", ".h")))
+OTHERS_STEPS = 0   # --others-steps: launch count for the other workloads (0: their own)
+
+
+def other_counts(steps, warmup):
+    """(steps, warmup) for one of the other workloads."""
+    return (OTHERS_STEPS, min(warmup, 2)) if OTHERS_STEPS > 0 else (steps, warmup)
 
 
 def read_traffic(workload_name, launch_count_hint=None):
@@ -186,7 +202,7 @@ def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=T
         if st != 0:
             raise RuntimeError(f"fa_fwd_gqa failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, _ = time_launches(launch, steps, 10)
+    m_step, m_kern, _ = time_launches(launch, *other_counts(steps, 10))
     flops = algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"{name}: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 {'causal' if causal else 'non-causal'}",
             "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
@@ -218,7 +234,7 @@ def time_decode(dev, stream_handle, B=8, H=32, H_kv=8, Nq=1, Nk=32768, d=128, ca
         if st != 0:
             raise RuntimeError(f"fa_decode failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, steps, 10)
+    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 10))
     cbytes = 2 * B * H_kv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
     splits = need // (B * H * Nq * (d + 1) * 4)
     return {"workload": f"decode: B={B} H={H} H_kv={H_kv} Nq={Nq} cache={Nk} d={d} bf16 "
@@ -256,7 +272,7 @@ def time_backward(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal
         if st != 0:
             raise RuntimeError(f"fa_bwd failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, steps, 5)
+    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 5))
     flops = 2.5 * algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"long_context_bwd: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 "
                         f"{'causal' if causal else 'non-causal'} (dQ, dK, dV)",
@@ -285,7 +301,7 @@ def time_fp8(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal=True
         if st != 0:
             raise RuntimeError(f"fa_fwd_fp8 failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, steps, 10)
+    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 10))
     flops = algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"long_context_fp8: B={B} H={H} H_kv={H_kv} N={N} d={d} e4m3 in, bf16 out "
                         f"{'causal' if causal else 'non-causal'}",
@@ -370,6 +386,51 @@ def summarize_traffic(fetch_csv, write_csv, workload_name, command):
     return path
 
 
+def summarize_traffic_all(fetch_csv, write_csv, command):
+    """Write profiles/traffic_all_kernels.txt: FETCH_SIZE and WRITE_SIZE per
+    dispatch of every kernel of a bench.py run, grouped by (kernel, grid size),
+    scaled to bytes by the calibration copy as in summarize_traffic."""
+    import csv
+
+    def load(path, counter):
+        groups, copy = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+                continue
+            if "fa::(anonymous namespace)::" not in r["Kernel_Name"]:
+                continue   # torch's own kernels (fills of test tensors)
+            name = r["Kernel_Name"].replace("void fa::(anonymous namespace)::", "").split("(fa::")[0]
+            groups.setdefault((name, int(r["Grid_Size"])), []).append(v)
+        return groups, max(copy)
+
+    fg, f_copy = load(fetch_csv, "FETCH_SIZE")
+    wg, w_copy = load(write_csv, "WRITE_SIZE")
+    mb = None
+    for tok in command.split("--calib-copy-mb")[1:]:
+        mb = int(tok.split()[0])
+    copy_bytes = mb * (1 << 20)
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    path = os.path.join(PROFILES, "traffic_all_kernels.txt")
+    with open(path, "w") as out:
+        out.write("# HBM traffic per dispatch of every kernel bench.py runs, by (kernel, grid size in threads)\n")
+        out.write("# two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE); KiB readings scaled to bytes by the same\n")
+        out.write(f"# counters on a device copy of {mb} MiB: fetch x{f_scale:.4f}, write x{w_scale:.4f}\n")
+        out.write(f"# command (each pass): {command}\n")
+        out.write(f"# kernel sources: {', '.join(os.path.basename(x) for x in TRAFFIC_ALL_SOURCES)} sha {source_hash(TRAFFIC_ALL_SOURCES)}\n")
+        out.write(f"{'kernel':52s} {'grid':>10s} {'n':>4s} {'fetch MB':>10s} {'write MB':>10s}\n")
+        for key in sorted(fg, key=lambda k: -sum(fg[k]) / len(fg[k])):
+            fv = sum(fg[key]) / len(fg[key]) * 1024.0 * f_scale / 1e6
+            wl = wg.get(key, [])
+            wv = sum(wl) / len(wl) * 1024.0 * w_scale / 1e6 if wl else float("nan")
+            out.write(f"{key[0]:52s} {key[1]:10d} {len(fg[key]):4d} {fv:10.2f} {wv:10.2f}\n")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,8 +444,18 @@ def main(argv=None):
                     help="also run one device copy of this many MiB (a known-size kernel for counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_<workload>.txt from two rocprofv3 --pmc CSV files and exit")
+    ap.add_argument("--summarize-traffic-all", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write profiles/traffic_all_kernels.txt from two rocprofv3 --pmc CSV files and exit")
+    ap.add_argument("--others-steps", type=int, default=0,
+                    help="time each of the other workloads with this many launches (0: their defaults)")
     args = ap.parse_args(argv)
 
+    if args.summarize_traffic_all:
+        print(summarize_traffic_all(*args.summarize_traffic_all))
+        return 0
+    if args.others_steps > 0:
+        global OTHERS_STEPS
+        OTHERS_STEPS = args.others_steps
     if args.summarize_traffic:
         from exact_io_aware_57_amd.inputs import workload
         print(summarize_traffic(*args.summarize_traffic[:2], workload(args.workload).name, args.summarize_traffic[2]))
@@ -427,7 +498,7 @@ def main(argv=None):
                 continue
             p = Problem(idx, dev)
             steps = 50 if w.N >= 4096 else 200
-            m_step, m_kern, m_min = time_launches(p.launcher(stream.cuda_stream), steps, 10)
+            m_step, m_kern, m_min = time_launches(p.launcher(stream.cuda_stream), *other_counts(steps, 10))
             entry = {"workload": w.describe(), "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
                      "tflops": round(p.flops / (m_kern * 1e-3) / 1e12, 2),
                      "hbm_gbs_compulsory": round(p.bytes / (m_kern * 1e-3) / 1e9, 1)}

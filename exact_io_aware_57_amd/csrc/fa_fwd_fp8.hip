@@ -13,15 +13,16 @@
 //    64 head-dimension elements per product (lane half h holds elements
 //    64 s + 32 h .. +31 of k-step s on both sides).
 //  * P: the row max is tracked exactly (the accumulator is rescaled whenever a
-//    row's max grows), so 0 <= P <= 1; P * 2^8 is rounded to e4m3 (round to
-//    nearest even; values down to 2^-14 keep 3 significant bits) and the 2^-8
-//    is folded into the final division.  The row sum l adds the float32 P.
+//    row's max grows), so 0 <= P <= 1; P * 2^8 (the factor folded into the
+//    exponent) is rounded to e4m3 (round to nearest even; values down to 2^-14
+//    keep 3 significant bits) and the 2^-8 comes out in the final division and
+//    the LSE.  The row sum l adds the float32 P * 2^8.
 //  * O^T += V^T P^T: the 64 keys of a tile are one product per 32 output
 //    columns.  Lane half h of P^T holds keys 32 kb + 8 g + 4 h + e (the keys
 //    its score registers hold), so V^T must supply the same keys: four
 //    transposing 8-bit LDS reads (ds_read_b64_tr_b8, 8 keys of one column per
 //    lane each) with per-lane row addresses that pick exactly those keys.
-//  * O = sv * O^T / (2^8 l) rounded to bf16; LSE = ln2 (m + log2 l).
+//  * O = sv * O^T / l rounded to bf16; LSE = ln2 (m - 8 + log2 l).
 // The workgroup is 4 waves x 32 query rows, K/V tiles of 64 keys double-
 // buffered in LDS by direct global->LDS loads, two workgroups per compute unit.
 #include <hip/hip_runtime.h>
@@ -211,6 +212,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
       rescale = true;
     }
     const float mref = m_run == -INFINITY ? 0.0f : m_run;
+    // exponentials of P * 2^8 directly (the 2^8 folded into the FMA's offset):
+    // the e4m3 operand needs no multiply, and l sums P * 2^8
+    const float mref8 = 8.0f - mref;
     // ---- P (float32, <= 1), row sum, and P * 2^8 as e4m3 in the slot order of
     // the second product: dword w holds registers 4 (w % 4) .. +3 of block w / 4
     float part[2][4];
@@ -221,10 +225,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
       for (int g = 0; g < 4; ++g) {
         float pr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][4 * g + e], sc, -mref));
+        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][4 * g + e], sc, mref8));
         part[kb][g] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0] * 256.0f, pr[1] * 256.0f, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2] * 256.0f, pr[3] * 256.0f, w, true);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
         pb[4 * kb + g] = w;
       }
     const float tsum = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) +
@@ -282,9 +286,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
     if (t + 1 < ntk) step(t + 1, stage1, stage0);
   }
 
-  // ---- epilogue: O = sv O^T / (2^8 l), LSE = ln2 (m + log2 l)
+  // ---- epilogue: O = sv O^T / l, LSE = ln2 (m - 8 + log2 l) (both sums carry 2^8)
   const float l = pair_sum(l_run);
-  const float inv = l > 0.0f ? p.descale_v / (256.0f * l) : 0.0f;
+  const float inv = l > 0.0f ? p.descale_v / l : 0.0f;   // l and O^T both carry the factor 2^8
   const int qi = qw0 + r32;
   if (qi < N) {
     __bf16* orow = Oh + (size_t)qi * D;
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
                          pack_bf16(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + col) = w;
       }
-    if (p.lse && hi == 0) p.lse[(size_t)bh * N + qi] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    if (p.lse && hi == 0) p.lse[(size_t)bh * N + qi] = l > 0.0f ? (m_run - 8.0f + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 

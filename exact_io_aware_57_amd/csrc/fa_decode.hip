@@ -126,9 +126,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
   for (int cb = 0; cb < DB; ++cb) oacc[cb] = f32x16{};
   float m_run = -INFINITY, l_run = 0.0f;
   const float sc = p.scale * kLog2e;
-  bf16x2 ones;
-  ones[0] = (__bf16)1.0f;
-  ones[1] = (__bf16)1.0f;
 
   auto tile = [&](int t) __attribute__((always_inline)) {
     const char* Ks = kbuf[t & 1];
@@ -174,15 +171,17 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[cb][e] *= alpha;
     uint32_t pk[KB][8];
+    float part[KB * 8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sc, -mref));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
+        part[kb * 8 + j] = p0 + p1;
         pk[kb][j] = pack_bf16(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][j]), ones, l_run, false);
       }
+    l_run += tree_sum(part);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int kb = i / (2 * DB), u = (i / DB) & 1, cb = i % DB;

@@ -64,6 +64,20 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum of v[0..N) (N a power of two) as a balanced tree, overwriting v.  The
+// softmax row sums use it on the float32 probabilities: plain adds, where a
+// v_dot2 over the packed bf16 values would run on the matrix pipeline at a
+// fraction of the VALU rate whenever another wave's products are running.
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&v)[N]) {
+  static_assert((N & (N - 1)) == 0, "power of two");
+#pragma unroll
+  for (int w = N / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+  return v[0];
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2 v;
   v[0] = (__bf16)a;  // round to nearest even (v_cvt_pk_bf16_f32)

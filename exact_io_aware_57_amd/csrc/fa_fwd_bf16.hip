@@ -30,8 +30,12 @@
 //    gfx950 transposing LDS read ds_read_b64_tr_b16.  Each lane again holds one
 //    query's outputs, so the softmax rescale is a per-lane scalar.
 //  * Non-matmul work per score: one FMA (scale and max subtraction folded), one
-//    v_exp_f32 (base 2), half a v_cvt_pk_bf16_f32 and half a v_dot2 (the row
-//    sum over the same bf16-rounded P that feeds the second product).  The
+//    v_exp_f32 (base 2), half a v_cvt_pk_bf16_f32 and the row sum: in the
+//    8-wave kernel one float32 add (a tree per tile over the unrounded P; the
+//    bf16-rounded P feeds the second product, so the weights sum to 1 within
+//    the 2^-9 of that rounding), in the 4-wave kernel half a v_dot2 over the
+//    rounded P.  v_dot2 runs on the matrix pipeline and slows several-fold
+//    next to another wave's products, which the 8-wave kernel always has.  The
 //    reference max of a row changes rarely: the 4-wave kernel moves it when a
 //    tile's max exceeds it by more than 2^8 in the exponent; the 8-wave kernel
 //    does not even compute a tile's max unless the tile's sum of P exceeds
@@ -228,6 +232,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
         rescale = true;
       }
       const float mref = (MASK && m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+      // this kernel keeps the row sum on v_dot2 over the packed P (measured
+      // faster here than float32 adds, unlike the 8-wave kernel)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -450,9 +456,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   f32x16 sacc[KB];
   uint32_t pk[KB][8];
   const float sc = p.scale * kLog2e;
-  bf16x2 ones;
-  ones[0] = (__bf16)1.0f;
-  ones[1] = (__bf16)1.0f;
 
   // MFMA phase: O^T = alpha O^T + V_{tv}^T P^T (if DO_PV) and S^T = K_{tk} Q^T
   // (if DO_QK).  The K operands are requested up front (the scheduling fence
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     // on the rare tiles where that sum is larger (or not a number, or the
     // row has no reference yet); those tiles are recomputed against it.
     auto exps = [&](float mref) __attribute__((always_inline)) {
-      float ls = 0.0f;
+      float part[KB * 8];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -581,10 +584,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j], sc, -mref));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
           const uint32_t pp = pack_bf16(p0, p1);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, ls, false);
+          part[kb * 8 + j] = p0 + p1;
           pk[kb][j] = pp;
         }
-      return ls;
+#pragma unroll
+      for (int w = KB * 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) part[i] = part[i] + part[i + w];
+      return part[0];
     };
     float ls = exps(m_run == -INFINITY ? 0.0f : m_run);
     const bool bad = !(ls <= kMaxTileSum) || m_run == -INFINITY;

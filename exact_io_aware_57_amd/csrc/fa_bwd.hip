@@ -136,20 +136,18 @@ __device__ __forceinline__ bf16x8 read_row(const char* tile, int rb, int blk, in
 }
 
 // A sequence of N products in order, product i taking the A operand rd(i):
-// each operand is read from LDS kAhead products before its product, so the
+// each operand is read from LDS AHEAD products before its product, so the
 // reads are in flight under the matrix work (a scheduling fence after every
 // product keeps the compiler from hoisting a whole tile's reads).
-constexpr int kAhead = 4;
-
-template <int N, typename RD, typename MF>
+template <int N, int AHEAD, typename RD, typename MF>
 __device__ __forceinline__ void products(RD rd, MF mf) {
-  bf16x8 ring[kAhead];
+  bf16x8 ring[AHEAD];
 #pragma unroll
-  for (int i = 0; i < kAhead && i < N; ++i) ring[i] = rd(i);
+  for (int i = 0; i < AHEAD && i < N; ++i) ring[i] = rd(i);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const bf16x8 a = ring[i % kAhead];
-    if (i + kAhead < N) ring[i % kAhead] = rd(i + kAhead);
+    const bf16x8 a = ring[i % AHEAD];
+    if (i + AHEAD < N) ring[i % AHEAD] = rd(i + AHEAD);
     mf(i, a);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -160,6 +158,9 @@ __device__ __forceinline__ void products(RD rd, MF mf) {
 template <int D>
 __device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char* dst, int wave, int lane) {
   using T = Tile<D, kBT>;
+  // the lane index through an empty asm: the per-lane addresses are recomputed
+  // at each tile instead of being held in registers across the loop
+  asm volatile("" : "+v"(lane));
 #pragma unroll
   for (int i = 0; i < T::NLD; ++i) {
     const int pos = (wave * T::NLD + i) * 64 + lane;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb) {
       // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-      products<2 * DC>(
+      products<2 * DC, 4>(
           [&](int i) __attribute__((always_inline)) { return i < DC ? read_row<D>(Qs, rb, qb, i) : read_row<D>(Gs, rb, qb, i - DC); },
           [&](int i, const bf16x8& a) __attribute__((always_inline)) {
             if (i < DC)
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         bp[u] = __builtin_bit_cast(bf16x8, u32x4{pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]});
         bs[u] = __builtin_bit_cast(bf16x8, u32x4{dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]});
       }
-      products<4 * DB>(
+      products<4 * DB, 4>(
           [&](int i) __attribute__((always_inline)) {
             return read_tr<D>((i & 1) ? Qs : Gs, tb0, tb1, qb, i / (2 * DB), (i / 2) % DB);
           },
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 // 3. dQ.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   using T = Tile<D, kBT>;
   constexpr int DC = T::DC, DB = T::DB;
   constexpr int STAGE = 2 * T::MAT;   // K, V
@@ -434,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
       f32x16 sacc = f32x16{}, pacc = f32x16{};
-      products<2 * DC>(
+      products<2 * DC, 2>(
           [&](int i) __attribute__((always_inline)) { return i < DC ? read_row<D>(Ks, rb, kb, i) : read_row<D>(Vs, rb, kb, i - DC); },
           [&](int i, const bf16x8& a) __attribute__((always_inline)) {
             if (i < DC)
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         bs[u] = __builtin_bit_cast(bf16x8, u32x4{dk[4 * u], dk[4 * u + 1], dk[4 * u + 2], dk[4 * u + 3]});
-      products<2 * DB>(
+      products<2 * DB, 2>(
           [&](int i) __attribute__((always_inline)) { return read_tr<D>(Ks, tb0, tb1, kb, i / DB, i % DB); },
           [&](int i, const bf16x8& a) __attribute__((always_inline)) {
             dqacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs[i / DB], dqacc[i % DB], 0, 0, 0);

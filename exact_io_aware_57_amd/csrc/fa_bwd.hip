@@ -36,9 +36,9 @@
 // operand of S, dP) and transposed (A operand of dK^T, dV^T, dQ^T, via
 // ds_read_b64_tr_b16), so their 16-byte chunks are stored with one XOR
 // swizzle that keeps both access patterns free of bank conflicts.
-// All three kernels run one wave per SIMD and keep the accumulators in the
+// The dK/dV kernel runs one wave per SIMD and keeps its accumulators in the
 // accumulation registers (this source is compiled without the VGPR-form
-// option).
+// option); the dQ kernel fits two waves per SIMD in 256 registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -465,6 +465,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   constexpr int NPV = KB * 2 * T::DB;   // MFMAs of O^T += V^T P^T per tile
   constexpr int NQK = KB * T::DC;       // MFMAs of S^T = K Q^T per tile
   auto mfma_phase = [&](const bool DO_PV, int tv, const bool DO_QK, int tk) __attribute__((always_inline)) {
+    // The wave in its matrix phase gets the higher issue priority of the two
+    // waves sharing its SIMD, so the partner's softmax instructions do not
+    // delay its products (measured: 1.915 -> 1.896 ms on the long context).
+    __builtin_amdgcn_s_setprio(1);
     // K operands are requested up front (they feed the longer S^T chain); the V
     // operands are read next to their products when the tile has more than one
     // key block, so the registers for all of them are not needed at once.
@@ -553,6 +557,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     for (int kb = 0; kb < KB; ++kb) pin(sacc[kb]);
 #pragma unroll
     for (int cb = 0; cb < T::DB; ++cb) pin(oacc[cb]);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Online softmax of sacc (tile t) into pk.  The mask, where the tile crosses
   // the valid-key end or this wave's causal diagonal, overwrites sacc in place.

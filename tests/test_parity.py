@@ -149,6 +149,81 @@ def test_large_grid_kernel(d, causal):
                        seed=d + causal)
 
 
+def check_full_heads(q, k, v, scale, causal, seqlens, heads, tag):
+    """Full-size call; every row of the listed (b, h) heads against the oracle.
+
+    Element bound 1e-2 + 2^-7 |O|: the absolute 1e-2 of the other tests covers
+    rows that average many values (|O| well below 1), while rows dominated by
+    one key have |O| up to max |V| (about 4 here), where rounding O to bf16
+    alone costs up to 2^-8 |O| and the bf16-rounded weights, normalised by the
+    sum of the unrounded ones, another 2^-9 |O| twice over."""
+    say(f"[parity] {tag}: q {tuple(q.shape)} k {tuple(k.shape)} causal={causal} "
+        f"seqlens={None if seqlens is None else seqlens.tolist()}")
+    o, lse = gpu_forward(q, k, v, scale, causal, seqlens)
+    assert torch.isfinite(o).all()
+    H, Hkv, N = q.shape[1], k.shape[1], q.shape[2]
+    worst, worst_l, total, count = 0.0, 0.0, 0.0, 0
+    for b, h in heads:
+        g = oracle.kv_head(h, H, Hkv)
+        sl = None if seqlens is None else seqlens[b:b + 1].numpy()
+        o_ref, lse_ref = oracle.attention_rows(np64(q[b:b + 1, h:h + 1]), np64(k[b:b + 1, g:g + 1]),
+                                               np64(v[b:b + 1, g:g + 1]), scale, causal, sl, 0, 0, np.arange(N))
+        og, lg = np64(o[b, h]), np64(lse[b, h])
+        e = np.abs(og - o_ref)
+        worst, total, count = max(worst, (e / (BF16_MAX + 2.0 ** -7 * np.abs(o_ref))).max()), total + e.sum(), count + e.size
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lg), fin)
+        assert np.all(og[~fin] == 0.0)
+        if fin.any():
+            worst_l = max(worst_l, np.abs(lg[fin] - lse_ref[fin]).max())
+    say(f"[parity] {tag}: O worst err/bound {worst:.3f} mean {total / count:.3e} LSE max {worst_l:.3e}")
+    assert worst <= 1.0 and total / count <= BF16_MEAN and worst_l <= BF16_LSE
+
+
+def ramp_keys(q, k, growth):
+    """Scores that grow along the keys: a shared direction u added to every query
+    and, with a weight rising linearly to ``growth``, to every key.  The row max
+    then moves up tile after tile, so the kernels must move their reference max
+    (and rescale what they have accumulated) many times per row."""
+    d, N = q.shape[-1], q.shape[-2]
+    u = torch.ones(d) / math.sqrt(d)
+    ramp = torch.linspace(0.0, growth, N)[:, None] * u
+    return (q.float() + 4.0 * u).to(q.dtype), (k.float() + ramp).to(k.dtype)
+
+
+# Grids large enough for the 8-wave kernel at head size 128 (query tiles of 256
+# rows): ragged lengths, padding, scores that keep rising (the rare path that
+# moves a row's reference max and rescales its accumulators); every row of a
+# few heads checked.
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_full_heads_ragged(d, causal):
+    B, H = (1, 256) if not causal else (2, 256)
+    for N in ((300, 511, 700) if not causal else (520, 777)):
+        q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=N + causal + d)
+        check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (0, 77), (B - 1, 255)],
+                         f"large grid full heads N={N} d={d}")
+
+
+def test_large_grid_full_heads_padding():
+    B, H, N = 6, 128, 600
+    q, k, v, _ = random_qkv(B, H, N, 128, torch.bfloat16, 1.0, seed=17)
+    sl = torch.tensor([0, 1, 63, 257, 599, 600], dtype=torch.int32)
+    for causal in (False, True):
+        check_full_heads(q, k, v, 0.0884, causal, sl, [(0, 3), (1, 5), (2, 0), (3, 127), (4, 64), (5, 9)],
+                         f"large grid full heads padding causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_full_heads_rising_scores(d, causal):
+    B, H, N = 2, 256, 1100
+    q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=23 + causal + d)
+    q, k = ramp_keys(q, k, 120.0)
+    check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (1, 200)],
+                     f"large grid full heads rising scores d={d}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("H,H_kv", [(8, 4), (8, 2), (6, 1)])

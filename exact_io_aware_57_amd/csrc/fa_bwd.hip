@@ -13,11 +13,11 @@
 //
 // Three kernels, no atomics, a fixed order of every sum (bitwise repeatable):
 //  1. bwd_rowdot_kernel: D_i = dO_i . O_i and lse2_i = LSE_i log2(e) per query
-//     row, into the caller's workspace (rows padded to a multiple of 64 per
+//     row, into the caller's workspace (rows padded to a multiple of 128 per
 //     head, the padding set to lse2 = +inf, D = 0).
 //  2. bwd_dkdv_kernel: one workgroup per (batch, key/value head, 128 keys);
 //     each wave holds its 32 keys' K and V rows as matrix operands and the
-//     transposed accumulators dV^T, dK^T, and streams 64-query tiles of Q, dO,
+//     transposed accumulators dV^T, dK^T, and streams 128-query tiles of Q, dO,
 //     lse2 and D (every query head of the group in turn) through LDS:
 //         S = Q K^T, P = exp2(S scale log2e - lse2), dP = dO V^T,
 //         dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
@@ -48,8 +48,9 @@
 namespace fa {
 namespace {
 
-constexpr int kBT = 64;         // rows of a streamed tile (queries in kernel 2, keys in kernel 3)
+constexpr int kBT = 64;         // rows of a loaded tile (two per query tile of kernel 2; the key tile of kernel 3)
 constexpr int kRowsWG = 128;    // rows held per workgroup (4 waves x 32)
+constexpr int kQT = 128;        // query rows per streamed tile of the dK/dV kernel
 
 // Swizzle for tiles read both as rows and transposed: chunk c of row r is stored
 // at c ^ swz(r).  Rows: 16 lanes read one chunk of 16 consecutive rows, which
@@ -178,7 +179,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   using T = Tile<D, kBT>;
   constexpr int DC = T::DC, DB = T::DB;
-  constexpr int STAGE = 2 * T::MAT + 2 * kBT * 4;   // Q, dO, lse2[64], D[64]
+  constexpr int QMAT = 2 * T::MAT;                  // one 128-row tile of Q or dO
+  constexpr int STAGE = 2 * QMAT + 2 * kQT * 4;      // Q, dO, lse2[128], D[128]
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
 
@@ -224,20 +226,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  const int nqt = (N + kBT - 1) / kBT;
-  const int qstart = CAUSAL ? k0 / kBT : 0;
+  const int nqt = (N + kQT - 1) / kQT;
+  const int qstart = CAUSAL ? k0 / kQT : 0;
   const int per_head = nqt - qstart;
   const int n_it = L > k0 ? G * per_head : 0;   // no valid key in this workgroup: nothing to accumulate
 
   auto issue_loads = [&](int it, char* base) __attribute__((always_inline)) {
     const int hq = g * G + it / per_head;
-    const int q0 = (qstart + it % per_head) * kBT;
+    const int q0 = (qstart + it % per_head) * kQT;
     const size_t hoff = ((size_t)b * p.H + hq) * (size_t)N * D;
     load_tile<D>(reinterpret_cast<const __bf16*>(p.q) + hoff, q0, N, base, wave, lane);
-    load_tile<D>(reinterpret_cast<const __bf16*>(p.dout) + hoff, q0, N, base + T::MAT, wave, lane);
-    if (wave < 2 && lane < 16) {   // 64 floats of lse2 (wave 0) or D (wave 1)
+    load_tile<D>(reinterpret_cast<const __bf16*>(p.q) + hoff, q0 + kBT, N, base + T::MAT, wave, lane);
+    load_tile<D>(reinterpret_cast<const __bf16*>(p.dout) + hoff, q0, N, base + QMAT, wave, lane);
+    load_tile<D>(reinterpret_cast<const __bf16*>(p.dout) + hoff, q0 + kBT, N, base + QMAT + T::MAT, wave, lane);
+    if (wave < 2 && lane < 32) {   // 128 floats of lse2 (wave 0) or D (wave 1)
       const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + hq) * (size_t)p.Npad + q0;
-      load_to_lds16(src + lane * 4, base + 2 * T::MAT + wave * kBT * 4);
+      load_to_lds16(src + lane * 4, base + 2 * QMAT + wave * kQT * 4);
     }
   };
 
@@ -252,13 +256,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   auto tile = [&](const bool MASK, const char* st, int q0) __attribute__((always_inline)) {
     const char* Qs = st;
-    const char* Gs = st + T::MAT;
-    const float* ls = reinterpret_cast<const float*>(st + 2 * T::MAT);
-    const float* ds = ls + kBT;
+    const char* Gs = st + QMAT;
+    const float* ls = reinterpret_cast<const float*>(st + 2 * QMAT);
+    const float* ds = ls + kQT;
     int rb = ad.row_base, tb0 = ad.tr_base0, tb1 = ad.tr_base1;
     asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQT / 32; ++qb) {
       // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       products<2 * DC, 4>(
@@ -319,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   auto step = [&](int it, const char* cur, char* next) __attribute__((always_inline)) {
     if (it + 1 < n_it) issue_loads(it + 1, next);
-    const int q0 = (qstart + it % per_head) * kBT;
-    const bool active = wave_live && (!CAUSAL || q0 + kBT - 1 >= kw0);
+    const int q0 = (qstart + it % per_head) * kQT;
+    const bool active = wave_live && (!CAUSAL || q0 + kQT - 1 >= kw0);
     if (active) {
-      const bool need_mask = (q0 + kBT > N) || (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
+      const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
       if (need_mask)
         tile(true, cur, q0);
       else
@@ -538,7 +542,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int bwd_row_pad() { return kBT; }
+int bwd_row_pad() { return kQT; }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   return p.d == 64 ? launch_all<64>(p, stream) : launch_all<128>(p, stream);

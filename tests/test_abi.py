@@ -186,10 +186,11 @@ def call_bwd(**over):
 
 def test_bwd_workspace_size(lib):
     f = binding.fa_bwd_workspace_size
-    # two floats per query row, rows of each head padded to a multiple of 64
+    # two floats per query row, rows of each head padded to a multiple of 128
     assert f(2, 8, 1000) == 2 * 2 * 8 * 1024 * 4
-    assert f(1, 1, 64) == 2 * 64 * 4
-    assert f(1, 1, 1) == 2 * 64 * 4
+    assert f(1, 1, 128) == 2 * 128 * 4
+    assert f(1, 1, 129) == 2 * 256 * 4
+    assert f(1, 1, 1) == 2 * 128 * 4
     assert f(0, 1, 1) == 0 and f(1, 0, 1) == 0 and f(1, 1, 0) == 0
 
 

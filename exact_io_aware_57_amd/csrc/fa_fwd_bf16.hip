@@ -727,6 +727,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
   const bool pp = pp_groups >= (p.causal ? 1024 : 256);
   if (p.d == 64) {
+    // At head size 64 the softmax outweighs the products and each phase's fixed
+    // costs (load issue, barrier) weigh more: long key ranges take 128-key
+    // tiles, which halve them per score (short ones lose more to the coarser
+    // last tile than they gain).
+    if (pp && p.N >= 2048) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
     if (pp) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }

@@ -205,6 +205,16 @@ def test_large_grid_full_heads_ragged(d, causal):
                          f"large grid full heads N={N} d={d}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_full_heads_long_keys_d64(causal):
+    # head size 64 with at least 2048 keys: the 8-wave kernel's 128-key tiles
+    B, H, N = 1, 128, 2100
+    q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=41 + causal)
+    check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (0, 127)], "large grid full heads d=64 N=2100")
+    q, k = ramp_keys(q, k, 120.0)
+    check_full_heads(q, k, v, 0.125, causal, None, [(0, 1)], "large grid full heads d=64 N=2100 rising scores")
+
+
 def test_large_grid_full_heads_padding():
     B, H, N = 6, 128, 600
     q, k, v, _ = random_qkv(B, H, N, 128, torch.bfloat16, 1.0, seed=17)

@@ -729,10 +729,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (p.d == 64) {
     // At head size 64 the softmax outweighs the products and each phase's fixed
     // costs (load issue, barrier) weigh more: long key ranges take 128-key
-    // tiles, which halve them per score (short ones lose more to the coarser
-    // last tile than they gain).
+    // tiles, which halve them per score, and short ones (under 1024 keys, a
+    // few tiles per workgroup) run faster on the 4-wave kernel with two
+    // workgroups per compute unit.
     if (pp && p.N >= 2048) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
-    if (pp) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
+    if (pp && p.N >= 1024) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }
   if (pp) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);

@@ -199,7 +199,7 @@ def ramp_keys(q, k, growth):
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_ragged(d, causal):
     B, H = (1, 256) if not causal else (2, 256)
-    for N in ((300, 511, 700) if not causal else (520, 777)):
+    for N in ((300, 511, 700, 1300) if not causal else (520, 777, 1300)):
         q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=N + causal + d)
         check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (0, 77), (B - 1, 255)],
                          f"large grid full heads N={N} d={d}")

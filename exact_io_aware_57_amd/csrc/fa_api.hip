@@ -62,7 +62,7 @@ int run(const fa::FwdParams& p, void* stream, bool bf16) {
   st = check_device();
   if (st != FA_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = !bf16 ? fa::launch_fwd_f32(p, s) : p.d == 256 ? fa::launch_fwd_bf16_d256(p, s) : fa::launch_fwd_bf16(p, s);
+  hipError_t e = !bf16 ? fa::launch_fwd_f32(p, s) : fa::launch_fwd_bf16(p, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -349,6 +349,11 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
 // K and V have two LDS buffers each.  At every even phase 2t the workgroup
 // issues the loads of K_{t+1} and V_t (direct global->LDS), and waits for them
 // at the end of phase 2t+1, before any wave reads them.
+// Head size 256 runs this kernel with 32-key tiles: Q fragments (64 registers),
+// O^T (128), the score tile (16) and P (8) then fit the 256 registers of a wave
+// at two waves per SIMD, provided the matrix phase reads each LDS operand two
+// products ahead of its use instead of a whole tile's operands up front, and
+// the tile loads recompute their addresses instead of holding them.
 // ---------------------------------------------------------------------------
 
 
@@ -434,18 +439,39 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     ld_kc[i] = (cst ^ kswz<D>(row)) * 8;
     ld_vc[i] = (cst ^ vswz<D>(row)) * 8;
   }
+  // At head size 256 the load addresses are recomputed at each tile from the
+  // lane index (passed through an empty asm) instead of being held.
+  auto ld_addr = [&](int i, int& row, int& kc, int& vc) __attribute__((always_inline)) {
+    if constexpr (D >= 256) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int pos = (wave * NLD + i) * 64 + ln;
+      row = pos / T::CH;
+      const int cst = pos % T::CH;
+      kc = (cst ^ kswz<D>(row)) * 8;
+      vc = (cst ^ vswz<D>(row)) * 8;
+    } else {
+      row = ld_row[i];
+      kc = ld_kc[i];
+      vc = ld_vc[i];
+    }
+  };
   auto load_k = [&](int t) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int key = min(t * BN + ld_row[i], N - 1);
-      dma16(Kh + (size_t)key * D + ld_kc[i], kbuf[t & 1] + (wave * NLD + i) * 1024);
+      int row, kc, vc;
+      ld_addr(i, row, kc, vc);
+      const int key = min(t * BN + row, N - 1);
+      dma16(Kh + (size_t)key * D + kc, kbuf[t & 1] + (wave * NLD + i) * 1024);
     }
   };
   auto load_v = [&](int t) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int key = min(t * BN + ld_row[i], N - 1);
-      dma16(Vh + (size_t)key * D + ld_vc[i], vbuf[t & 1] + (wave * NLD + i) * 1024);
+      int row, kc, vc;
+      ld_addr(i, row, kc, vc);
+      const int key = min(t * BN + row, N - 1);
+      dma16(Vh + (size_t)key * D + vc, vbuf[t & 1] + (wave * NLD + i) * 1024);
     }
   };
 
@@ -469,6 +495,60 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
     // waves sharing its SIMD, so the partner's softmax instructions do not
     // delay its products (measured: 1.915 -> 1.896 ms on the long context).
     __builtin_amdgcn_s_setprio(1);
+    if constexpr (D >= 256) {
+      // Head size 256: no room for a tile's operands at once; each operand is
+      // read two products ahead of its use.
+      const char* Ks2 = kbuf[tk & 1];
+      const char* Vs2 = vbuf[tv & 1];
+      int kb0 = kbase, vb0 = vbase;
+      asm volatile("" : "+v"(kb0), "+v"(vb0));
+      if (DO_QK) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+        auto read_k = [&](int i) __attribute__((always_inline)) {
+          return *reinterpret_cast<const u32x4*>(Ks2 + (i % KB) * 32 * T::ROW + (kb0 ^ ((i / KB) << 5)));
+        };
+        u32x4 kr[2];
+        kr[0] = read_k(0);
+        kr[1] = read_k(1);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+          const u32x4 a = kr[i & 1];
+          if (i + 2 < NQK) kr[i & 1] = read_k(i + 2);
+          sacc[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[i / KB], sacc[i % KB], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (DO_PV) {
+        auto read_v = [&](int i, s16x4& lo, s16x4& hv) __attribute__((always_inline)) {
+          const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+          const char* vb = Vs2 + (kb * 32 + 16 * u) * T::ROW + (vb0 ^ (cb << 6));
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+          hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * T::ROW));
+        };
+        s16x4 vl[2], vh[2];
+        read_v(0, vl[0], vh[0]);
+        read_v(1, vl[1], vh[1]);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          const int kb = i / (2 * T::DB), u = (i / T::DB) & 1, cb = i % T::DB;
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, vl[i & 1]);
+          const u32x2 hi2 = __builtin_bit_cast(u32x2, vh[i & 1]);
+          const u32x4 a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          if (i + 2 < NPV) read_v(i + 2, vl[i & 1], vh[i & 1]);
+          const u32x4 b4 = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), __builtin_bit_cast(bf16x8, b4),
+                                                             oacc[cb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) pin(sacc[kb]);
+#pragma unroll
+      for (int cb = 0; cb < T::DB; ++cb) pin(oacc[cb]);
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     // K operands are requested up front (they feed the longer S^T chain); the V
     // operands are read next to their products when the tile has more than one
     // key block, so the registers for all of them are not needed at once.
@@ -726,6 +806,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   // kernel with 128 rows per workgroup and two workgroups per compute unit.
   const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
   const bool pp = pp_groups >= (p.causal ? 1024 : 256);
+  if (p.d == 256) {
+    // 32-key tiles: the score tile, the Q fragments (64 registers) and O^T (128)
+    // of a wave then fit two waves per SIMD.  Smaller grids use the one-wave-
+    // per-SIMD head-size-256 kernel with 128 query rows per workgroup.
+    if (pp) return p.causal ? launch_pp<256, 32, true>(p, stream) : launch_pp<256, 32, false>(p, stream);
+    return launch_fwd_bf16_d256(p, stream);
+  }
   if (p.d == 64) {
     // At head size 64 the softmax outweighs the products and each phase's fixed
     // costs (load issue, barrier) weigh more: long key ranges take 128-key

@@ -9,10 +9,13 @@
 // fragments of one wave's 32 query rows take 64 registers and its transposed
 // output accumulator O^T (256 x 32 fp32) 128, so two waves per SIMD (256
 // registers each) cannot hold them with the score tile and the operand
-// buffers.  This kernel therefore runs one wave per SIMD (4 waves per compute
-// unit) and uses that wave's whole 512-entry register file: it is compiled
-// without the option that keeps MFMA accumulators in ordinary VGPRs, so S^T
-// and O^T live in the accumulation registers.
+// buffers at 64-key tiles.  This kernel therefore runs one wave per SIMD (4
+// waves per compute unit) and uses that wave's whole 512-entry register file:
+// it is compiled without the option that keeps MFMA accumulators in ordinary
+// VGPRs, so S^T and O^T live in the accumulation registers.  It serves grids
+// too small for the 8-wave ping-pong kernel, which takes head size 256 with
+// 32-key tiles on larger grids (two waves per SIMD hide each other's tile
+// loads and softmax).
 //
 //  * Workgroup: 4 waves x 32 query rows of one (batch, head); K/V tiles of 64
 //    keys (32 KB each at d = 256), double-buffered in LDS (128 KB) and filled by

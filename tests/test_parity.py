@@ -195,7 +195,7 @@ def ramp_keys(q, k, growth):
 # rows): ragged lengths, padding, scores that keep rising (the rare path that
 # moves a row's reference max and rescales its accumulators); every row of a
 # few heads checked.
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_ragged(d, causal):
     B, H = (1, 256) if not causal else (2, 256)
@@ -215,16 +215,17 @@ def test_large_grid_full_heads_long_keys_d64(causal):
     check_full_heads(q, k, v, 0.125, causal, None, [(0, 1)], "large grid full heads d=64 N=2100 rising scores")
 
 
-def test_large_grid_full_heads_padding():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_large_grid_full_heads_padding(d):
     B, H, N = 6, 128, 600
-    q, k, v, _ = random_qkv(B, H, N, 128, torch.bfloat16, 1.0, seed=17)
+    q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=17 + d)
     sl = torch.tensor([0, 1, 63, 257, 599, 600], dtype=torch.int32)
     for causal in (False, True):
-        check_full_heads(q, k, v, 0.0884, causal, sl, [(0, 3), (1, 5), (2, 0), (3, 127), (4, 64), (5, 9)],
-                         f"large grid full heads padding causal={causal}")
+        check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, sl, [(0, 3), (1, 5), (2, 0), (3, 127), (4, 64), (5, 9)],
+                         f"large grid full heads padding causal={causal} d={d}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_rising_scores(d, causal):
     B, H, N = 2, 256, 1100

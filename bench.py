@@ -431,6 +431,63 @@ def summarize_traffic_all(fetch_csv, write_csv, command):
     return path
 
 
+COUNTER_UTIL = ["MfmaUtil", "VALUBusy", "LdsUtil", "LdsBankConflict"]
+COUNTER_INSTS = ["SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_LDS_DATA_FIFO_FULL",
+                 "SQ_WAIT_INST_LDS"]
+
+
+def summarize_counters(util_csv, insts_csv, command):
+    """Write profiles/counters_all_kernels.txt from two rocprofv3 --pmc runs of
+    bench.py: rocprofv3's derived MfmaUtil, VALUBusy, LdsUtil and
+    LdsBankConflict, and raw SQ instruction counts, averaged over the
+    dispatches of each (kernel, grid size)."""
+    import csv
+
+    def load(path):
+        groups = {}
+        for r in csv.DictReader(open(path)):
+            if "fa::(anonymous namespace)::" not in r["Kernel_Name"]:
+                continue   # torch's own kernels (fills of test tensors)
+            name = r["Kernel_Name"].replace("void fa::(anonymous namespace)::", "").split("(fa::")[0]
+            key = (name, int(r["Grid_Size"]))
+            groups.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return groups
+
+    def mean(xs):
+        return sum(xs) / len(xs) if xs else float("nan")
+
+    util, insts = load(util_csv), load(insts_csv)
+    keys = sorted(set(util) | set(insts), key=lambda k: -mean(util.get(k, {}).get("MfmaUtil", [0.0])))
+    path = os.path.join(PROFILES, "counters_all_kernels.txt")
+    with open(path, "w") as out:
+        out.write("# Utilisation counters of every kernel bench.py runs, by (kernel, grid size in threads), averaged\n")
+        out.write("# over the profiled dispatches (n).  Two rocprofv3 --pmc runs, <counters> first\n")
+        out.write(f"# '{' '.join(COUNTER_UTIL)}', then '{' '.join(COUNTER_INSTS)}':\n")
+        out.write(f"#   {command}\n")
+        out.write("# rocprofv3's formulas for the derived counters (its gfx950 counter list):\n")
+        out.write("#   MfmaUtil        = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD_NUM)\n")
+        out.write("#   VALUBusy        = 100 * sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE)\n")
+        out.write("#   LdsUtil         = 100 * sum(SQ_LDS_IDX_ACTIVE) / (max(GRBM_GUI_ACTIVE) * CU_NUM)\n")
+        out.write("#   LdsBankConflict = sum(SQ_LDS_BANK_CONFLICT) / (sum(SQ_LDS_IDX_ACTIVE) - sum(SQ_LDS_BANK_CONFLICT))\n")
+        out.write("# MfmaUtil counts every issued product (masked causal diagonal products included) and pipeline busy\n")
+        out.write("# cycles, so it reads above the algorithmic-FLOP fraction of peak.  Instruction counts are per\n")
+        out.write("# dispatch in wave instructions; the VALU count includes MFMA and transcendental instructions.\n")
+        out.write(f"# kernel sources: {', '.join(os.path.basename(x) for x in TRAFFIC_ALL_SOURCES)} "
+                  f"sha {source_hash(TRAFFIC_ALL_SOURCES)}\n")
+        out.write(f"{'kernel':40s} {'grid':>8s} {'n':>3s} " + " ".join(f"{c:>15s}" for c in COUNTER_UTIL) + "\n")
+        for key in keys:
+            u = util.get(key, {})
+            vals = [mean(u.get(c, [])) for c in COUNTER_UTIL]
+            out.write(f"{key[0]:40s} {key[1]:8d} {len(u.get('MfmaUtil', [])):3d} "
+                      + " ".join(f"{v:15.4f}" for v in vals) + "\n")
+        out.write("\n")
+        out.write(f"{'kernel':40s} {'grid':>8s} " + " ".join(f"{c[3:]:>18s}" for c in COUNTER_INSTS) + "\n")
+        for key in keys:
+            i = insts.get(key, {})
+            out.write(f"{key[0]:40s} {key[1]:8d} " + " ".join(f"{mean(i.get(c, [])):18.0f}" for c in COUNTER_INSTS) + "\n")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,8 +505,13 @@ def main(argv=None):
                     help="write profiles/traffic_all_kernels.txt from two rocprofv3 --pmc CSV files and exit")
     ap.add_argument("--others-steps", type=int, default=0,
                     help="time each of the other workloads with this many launches (0: their defaults)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("UTIL_CSV", "INSTS_CSV", "COMMAND"),
+                    help="write profiles/counters_all_kernels.txt from two rocprofv3 --pmc CSV files and exit")
     args = ap.parse_args(argv)
 
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return 0
     if args.summarize_traffic_all:
         print(summarize_traffic_all(*args.summarize_traffic_all))
         return 0

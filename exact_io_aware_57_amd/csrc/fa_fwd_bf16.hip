@@ -800,30 +800,40 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  // The ping-pong kernel (8 waves, 256 query rows per workgroup) needs at least
-  // one workgroup per compute unit (256 on MI355X), and for causal problems,
-  // whose workgroups differ in length, several; smaller problems use the 4-wave
-  // kernel with 128 rows per workgroup and two workgroups per compute unit.
+  // Kernel choice by head size, key range and grid size (workgroups of the
+  // ping-pong kernel: 256 query rows each), from same-process timings of every
+  // candidate on gfx950 over grids of 32 to 2048 such workgroups.
   const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
   const bool pp = pp_groups >= (p.causal ? 1024 : 256);
   if (p.d == 256) {
     // 32-key tiles: the score tile, the Q fragments (64 registers) and O^T (128)
-    // of a wave then fit two waves per SIMD.  Smaller grids use the one-wave-
-    // per-SIMD head-size-256 kernel with 128 query rows per workgroup.
-    if (pp) return p.causal ? launch_pp<256, 32, true>(p, stream) : launch_pp<256, 32, false>(p, stream);
+    // of a wave then fit two waves per SIMD.  On grids of 256 (non-causal) and
+    // 512 (causal) workgroups the ping-pong kernel takes 11-29% less time than
+    // the one-wave-per-SIMD head-size-256 kernel (128 query rows per
+    // workgroup), which takes 12-18% less on grids of 64 and 128.
+    if (pp_groups >= 256) return p.causal ? launch_pp<256, 32, true>(p, stream) : launch_pp<256, 32, false>(p, stream);
     return launch_fwd_bf16_d256(p, stream);
   }
   if (p.d == 64) {
-    // At head size 64 the softmax outweighs the products and each phase's fixed
-    // costs (load issue, barrier) weigh more: long key ranges take 128-key
-    // tiles, which halve them per score, and short ones (under 1024 keys, a
-    // few tiles per workgroup) run faster on the 4-wave kernel with two
-    // workgroups per compute unit.
-    if (pp && p.N >= 2048) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
+    // At head size 64 the softmax outweighs the products and each tile's fixed
+    // costs (load issue, barriers) weigh more, so long key ranges take 128-key
+    // tiles, which halve them per score.  The ping-pong kernel needs a full
+    // grid: 256 workgroups, and causal grids need 4096 keys or more (at 2048
+    // causal keys the 4-wave kernel takes 11-13% less time even at 2048
+    // workgroups).  Elsewhere the 4-wave kernel (128 rows per workgroup, two
+    // workgroups per compute unit) runs 128-key tiles from 2048 keys up (3-12%
+    // less time than 64-key tiles on grids under 1024 workgroups, within 3%
+    // above) and 64-key tiles below, where a workgroup sees only a few tiles.
+    const bool pp_long = p.causal ? (pp_groups >= 256 && p.N >= 4096) : (pp_groups >= 256 && p.N >= 2048);
+    if (pp_long) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
+    if (p.N >= 2048) return p.causal ? launch<64, 1, 128, 2, true>(p, stream) : launch<64, 1, 128, 2, false>(p, stream);
     if (pp && p.N >= 1024) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }
-  if (pp) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
+  // Head size 128: the ping-pong kernel from 1024 keys up at any grid size
+  // (4-28% less time than the 4-wave kernel on grids of 32 to 512 workgroups,
+  // causal or not), and on full grids below that.
+  if (pp || p.N >= 1024) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
   return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }
 

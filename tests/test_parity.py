@@ -138,8 +138,10 @@ def check_sampled_rows(q, k, v, scale, causal, seqlens, heads, tag, n_rows=40, s
     assert worst <= BF16_MAX and total / count <= BF16_MEAN and worst_l <= BF16_LSE
 
 
-# Grids large enough for the 8-wave kernel (at least 256 workgroups of 256 rows,
-# 1024 when causal); the small shapes elsewhere in this file run the 4-wave one.
+# Grids large enough for the 8-wave kernel at head size 64 (at least 256
+# workgroups of 256 rows; causal: 4096 keys or more); head size 128 takes it
+# from 1024 keys up at any grid size.  The small shapes elsewhere in this file
+# run the 4-wave kernel.
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_kernel(d, causal):
@@ -207,12 +209,49 @@ def test_large_grid_full_heads_ragged(d, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_long_keys_d64(causal):
-    # head size 64 with at least 2048 keys: the 8-wave kernel's 128-key tiles
+    # head size 64 with at least 2048 keys: 128-key tiles, in the 8-wave kernel
+    # (non-causal) or in the 4-wave kernel (causal heads under 4096 keys)
     B, H, N = 1, 128, 2100
     q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=41 + causal)
     check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (0, 127)], "large grid full heads d=64 N=2100")
     q, k = ramp_keys(q, k, 120.0)
     check_full_heads(q, k, v, 0.125, causal, None, [(0, 1)], "large grid full heads d=64 N=2100 rising scores")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_keys_full_heads_d64_small_grid(causal):
+    """Head size 64, 2048 keys or more, fewer than 256 workgroups: the 4-wave
+    kernel with 128-key tiles; ragged tail, padding and rising scores."""
+    B, H, N = 2, 4, 2100
+    q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=51 + causal)
+    check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (1, 3)], "4-wave 128-key tiles d=64 N=2100")
+    sl = torch.tensor([2049, 700], dtype=torch.int32)
+    check_full_heads(q, k, v, 0.125, causal, sl, [(0, 1), (1, 2)], "4-wave 128-key tiles d=64 N=2100 padding")
+    q, k = ramp_keys(q, k, 120.0)
+    check_full_heads(q, k, v, 0.125, causal, None, [(1, 0)], "4-wave 128-key tiles d=64 N=2100 rising scores")
+
+
+def test_long_keys_full_heads_d64_causal_large_grid():
+    """Causal head size 64 with 4096 keys or more on 256 workgroups or more:
+    the 8-wave kernel's 128-key tiles; every row of two heads."""
+    B, H, N = 1, 16, 4100
+    q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=57)
+    check_full_heads(q, k, v, 0.125, True, None, [(0, 0), (0, 15)], "8-wave 128-key tiles causal d=64 N=4100")
+    q, k = ramp_keys(q, k, 120.0)
+    check_full_heads(q, k, v, 0.125, True, None, [(0, 7)], "8-wave 128-key tiles causal d=64 N=4100 rising scores")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_keys_full_heads_d128_tiny_grid(causal):
+    """Head size 128 from 1024 keys up runs the 8-wave kernel on any grid, down
+    to a few workgroups: every row of each head, ragged tails and padding."""
+    for N in (1024, 1500, 2100):
+        q, k, v, _ = random_qkv(1, 2, N, 128, torch.bfloat16, 1.0, seed=61 + N + causal)
+        check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, None, [(0, 0), (0, 1)],
+                         f"8-wave d=128 tiny grid N={N}")
+    q, k, v, _ = random_qkv(2, 1, 1500, 128, torch.bfloat16, 1.0, seed=67 + causal)
+    sl = torch.tensor([1025, 300], dtype=torch.int32)
+    check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, sl, [(0, 0), (1, 0)], "8-wave d=128 tiny grid padding")
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -261,12 +300,15 @@ def test_grouped_query_large_grid(d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_head_size_256_large_grid(causal):
-    """Head size 256 on a grid of many workgroups (its own kernel at every size):
-    sampled rows of several heads against the oracle, and bitwise repeatable."""
-    B, H, N = 2, 8, 4096
+@pytest.mark.parametrize("B,H", [(2, 8), (1, 4)])
+def test_head_size_256_large_grid(B, H, causal):
+    """Head size 256 with 4096 keys: 256 workgroups run the 8-wave kernel with
+    32-key tiles, 64 the one-wave-per-SIMD head-size-256 kernel; sampled rows of
+    several heads against the oracle, and bitwise repeatable."""
+    N = 4096
     q, k, v, _ = random_qkv(B, H, N, 256, torch.bfloat16, 0.5, seed=90 + causal)
-    check_sampled_rows(q, k, v, 1.0 / 16.0, causal, None, [(0, 0), (1, 3), (1, 7)], "d=256 large", seed=causal)
+    check_sampled_rows(q, k, v, 1.0 / 16.0, causal, None, [(0, 0), (B - 1, 3), (B - 1, H - 1)], f"d=256 B={B} H={H}",
+                       seed=causal)
     o1, l1 = gpu_forward(q, k, v, 1.0 / 16.0, causal, None)
     o2, l2 = gpu_forward(q, k, v, 1.0 / 16.0, causal, None)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -213,7 +213,9 @@ const char* fa_status_str(int status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_INVALID_ARG:
       return "FA_ERR_INVALID_ARG: null tensor, non-positive size, key/value heads not dividing heads, bad scale or size overflow";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension not 64/128, or device is not gfx950";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: head dimension not supported by this entry point (64, 128, or 256 for the "
+             "forward pass), or device is not gfx950";
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte alignment, lse/seqlens 4-byte";
     case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no current HIP device";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";

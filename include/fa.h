@@ -73,7 +73,10 @@ typedef enum fa_status {
  *   stream  : hipStream_t to enqueue on, or NULL
  * Arithmetic: S = Q K^T and O += P V on bf16 matrix cores with float32
  * accumulation; softmax statistics in float32; P is rounded to bf16 for the
- * second product and the row sum is taken over the same rounded P.
+ * second product.  The row sum is taken over that rounded P in the kernels for
+ * partial grids and short key ranges, and over the float32 P before rounding
+ * in the 8-wave kernel for full grids and long key ranges (the weights then
+ * sum to 1 within 2^-9).
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -284,6 +284,16 @@ def test_grouped_query_parity(H, H_kv, d, causal):
                              tag=f"grouped H={H} H_kv={H_kv} n={n} d={d}")
 
 
+@pytest.mark.parametrize("d,N", [(64, 2100), (128, 1500)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_query_long_keys_small_grid(d, N, causal):
+    """Grouped heads on the paths small grids take with long key ranges: the
+    4-wave kernel's 128-key tiles (d = 64) and the 8-wave kernel (d = 128)."""
+    q, k, v, seqlens = random_qkv_grouped(2, 4, 2, N, d, torch.bfloat16, 1.0, seed=80 + d + causal, len_range=(N // 2, N))
+    check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, seqlens, [(0, 0), (0, 3), (1, 1)],
+                     f"grouped long keys small grid d={d} N={N}")
+
+
 def test_grouped_query_fp32():
     q, k, v, seqlens = random_qkv_grouped(2, 4, 2, 150, 64, torch.float32, 1.0, seed=5, len_range=(20, 150))
     check_against_oracle(q, k, v, 0.125, True, seqlens, fp32=True, tag="grouped fp32")

@@ -43,8 +43,8 @@
 //    P may reach 2^8 in between).  The output is divided by the row sum once
 //    at the end.
 //  * Masks are applied only on tiles that straddle a boundary (causal diagonal,
-//    last valid key), in a separate instantiation of the tile body; tiles wholly
-//    above a wave's causal diagonal are skipped.
+//    last valid key), by a branch that overwrites the score tile in place;
+//    tiles wholly above a wave's causal diagonal are skipped.
 //  * Workgroups are renumbered so that each XCD (each its own L2) receives a
 //    contiguous run of (head, query tile) pairs, and causal query tiles are
 //    issued heaviest first.
@@ -178,8 +178,13 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
   ones[0] = (__bf16)1.0f;
   ones[1] = (__bf16)1.0f;
 
-  // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-  auto tile = [&](const bool MASK, const char* Ks, int k0) __attribute__((always_inline)) {
+  // One K/V tile: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.  One
+  // body serves masked and unmasked tiles (the mask overwrites the score tile
+  // in place under a runtime branch) and the rare rescale multiplies O^T before
+  // the one copy of the second product: with separate inlined bodies per case
+  // O^T sits in different registers on each path and the compiler copies all
+  // of it at the join (16-32 v_mov_b64 per tile); results are bitwise the same.
+  auto tile = [&](const char* Ks, int k0) __attribute__((always_inline)) {
     const char* Vs = Ks + T::MAT;
 
     // S^T: lane holds S[q = qw0 + 32qb + r32][k0 + 32kb + 8(r/4) + 4hi + r%4].
@@ -202,9 +207,10 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
     uint32_t pk[QB][KB][8];   // P^T as packed bf16 pairs (accumulator registers 2j, 2j+1)
     float alpha[QB];
     bool rescale = false;     // wave-uniform: some row max moved by more than 2^kTau
+    const bool mask = (k0 + BN > kv_valid) || (CAUSAL && k0 + BN - 1 > qw0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (MASK) {
+      if (mask) {
         const int qi = qw0 + qb * 32 + r32;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
         m_run[qb] = m_new;
         rescale = true;
       }
-      const float mref = (MASK && m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+      const float mref = (mask && m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
       // this kernel keeps the row sum on v_dot2 over the packed P (measured
       // faster here than float32 adds, unlike the 8-wave kernel)
 #pragma unroll
@@ -249,8 +255,6 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
     // O^T = alpha O^T + V^T P^T.  MFMA (kb, u) takes accumulator registers
     // 8u..8u+7 of block kb, i.e. keys 32kb + 16u + {0..3, 8..11} + 4hi; the A
     // operand supplies the same keys as two transposing reads of 4 rows each.
-    // The rare rescale and the product sit in one branch so that both paths
-    // end in MFMAs writing the same accumulators.
     auto pv = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -282,10 +286,8 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
         for (int cb = 0; cb < T::DB; ++cb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha[qb];
-      pv();
-    } else {
-      pv();
     }
+    pv();
   };
 
   // One step: start the loads of tile t+1 into `next`, compute tile t from
@@ -294,13 +296,7 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
     if (t + 1 < ntk) issue_loads(t + 1, next);
     const int k0 = t * BN;
     const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
-    if (active) {
-      const bool need_mask = (k0 + BN > kv_valid) || (CAUSAL && k0 + BN - 1 > qw0);
-      if (need_mask)
-        tile(true, cur, k0);
-      else
-        tile(false, cur, k0);
-    }
+    if (active) tile(cur, k0);
     wait_vmem();
     __syncthreads();
   };

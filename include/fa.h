@@ -150,7 +150,8 @@ size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, i
  *   d        : 64 or 128;  descales: finite and > 0;  other arguments as fa_fwd_gqa
  * FlashAttention (UR), section "FlashAttention-3 (2024)", names FP8 support.
  * Arithmetic: S = Q K^T on 8-bit matrix cores with float32 accumulation; the
- * softmax in float32 with the exact running row max; P scaled by 2^8 and
+ * softmax in float32 with a reference row max that moves only when a tile's
+ * max exceeds it by more than 2^0.75, so P <= 2^0.75; P scaled by 2^8 and
  * rounded to e4m3 (relative error <= 2^-4) for O += P V on 8-bit matrix cores;
  * the row sum l adds the float32 P.  Returns FA_OK or a negative fa_status;
  * nothing is enqueued on error.

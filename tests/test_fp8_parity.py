@@ -125,6 +125,23 @@ def test_fp8_descales_and_peaked_scores():
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("growth", [0.5, 3.0])
+def test_fp8_rising_scores(growth, causal):
+    """Scores that grow along the keys (a ramp added to every key element): the
+    reference max moves many times per row, and between moves P climbs towards
+    its ceiling of 2^0.75 (P * 2^8 near the largest e4m3 value).  The slow ramp
+    (about 0.4 in the base-2 exponent per 64-key tile) lets P accumulate below
+    the threshold; the fast one moves the reference on almost every tile."""
+    B, H, N, d = 1, 2, 1000, 64
+    g = torch.Generator().manual_seed(77 + causal + int(growth))
+    q = torch.randn(B, H, N, d, generator=g) * 0.5 + 1.0
+    k = torch.randn(B, H, N, d, generator=g) * 0.5 + torch.linspace(0.0, growth, N)[:, None]
+    v = torch.randn(B, H, N, d, generator=g)
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous() for x in (q, k, v))
+    check(q8, k8, v8, (1.0, 1.0, 1.0), 0.125, causal, None, f"rising scores growth={growth}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp8_large_grid(causal):
     """Many workgroups per head (sampled rows, every row checked for finiteness),
     and bitwise repeatable."""

@@ -36,11 +36,11 @@
 //    the 2^-9 of that rounding), in the 4-wave kernel half a v_dot2 over the
 //    rounded P.  v_dot2 runs on the matrix pipeline and slows several-fold
 //    next to another wave's products, which the 8-wave kernel always has.  The
-//    reference max of a row changes rarely: the 4-wave kernel moves it when a
-//    tile's max exceeds it by more than 2^8 in the exponent; the 8-wave kernel
-//    does not even compute a tile's max unless the tile's sum of P exceeds
-//    2^8, which every P <= 2^8 rules out (the result is the same either way;
-//    P may reach 2^8 in between).  The output is divided by the row sum once
+//    reference max of a row changes rarely: the kernels do not even compute a
+//    tile's max unless the tile's sum of P exceeds 2^8, which every P <= 2^8
+//    rules out (P may reach 2^8 in between); the 4-wave kernel with 128-key
+//    tiles at head size 64 instead computes each tile's max and moves the
+//    reference when the max exceeds it by more than 2^8 in the exponent.  The output is divided by the row sum once
 //    at the end.
 //  * Masks are applied only on tiles that straddle a boundary (causal diagonal,
 //    last valid key), by a branch that overwrites the score tile in place;
@@ -62,6 +62,11 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
   using T = Tile<D, BN>;
   constexpr int KB = T::KB;
   constexpr int QW = 32 * QB;             // query rows per wave
+  // Max-free softmax (below) on every instantiation but 128-key tiles at head
+  // size 64, where computing the tile's max measured faster (BERT- and GPT-2-
+  // shaped 0.0265 -> 0.0254 and 0.0341 -> 0.0327 ms; at 2048 keys with 128-key
+  // tiles 2-4% slower).
+  constexpr bool kMaxFree = !(D == 64 && BN == 128);
   constexpr int BM = kWaves * QW;         // query rows per workgroup
   // Two K/V stages as separate LDS objects, so the compiler can tell that the
   // direct loads into one stage never alias the reads of the other.
@@ -221,6 +226,47 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
             sacc[qb][kb][r] = ok ? sacc[qb][kb][r] : -INFINITY;
           }
       }
+      alpha[qb] = 1.0f;
+      if constexpr (kMaxFree) {
+        // Exponentials against the current reference max without computing
+        // the tile's max (as in the 8-wave kernel): every p is at most 2^kTau
+        // whenever the tile's sum of p is; the max is computed, and the tile
+        // redone against it, only when the sum is larger, not a number, or the
+        // row has no reference yet.
+        auto exps = [&](float mref) __attribute__((always_inline)) {
+          float ts = 0.0f;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j], sc, -mref));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
+              const uint32_t pp = pack_bf16(p0, p1);
+              ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, ts, false);
+              pk[qb][kb][j] = pp;
+            }
+          return ts;
+        };
+        float ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]);
+        const bool bad = !(ls <= kMaxTileSum) || m_run[qb] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+          keep_branch();
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+          mx = pair_max(mx);
+          const float m_new = fmaxf(m_run[qb], mx * sc);
+          alpha[qb] = (m_run[qb] == -INFINITY || m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          l_run[qb] *= alpha[qb];
+          m_run[qb] = m_new;
+          rescale = true;
+          ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]);
+        }
+        l_run[qb] += ls;
+        continue;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -229,7 +275,6 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
       mx = pair_max(mx);
       const float tmax = mx * sc;
       const bool need = tmax > m_run[qb] + kTau;
-      alpha[qb] = 1.0f;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float m_new = need ? tmax : m_run[qb];
         alpha[qb] = (m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);

@@ -231,6 +231,21 @@ def test_long_keys_full_heads_d64_small_grid(causal):
     check_full_heads(q, k, v, 0.125, causal, None, [(1, 0)], "4-wave 128-key tiles d=64 N=2100 rising scores")
 
 
+@pytest.mark.parametrize("d,N", [(64, 1000), (128, 700)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_grid_rising_scores(d, N, causal):
+    """The 4-wave kernel with 64-key tiles (head size 64) and 32-key tiles (head
+    size 128) on small grids, with scores that rise along the keys: the tile
+    sums of P keep exceeding 2^8, so the tile max is computed and the reference
+    moved many times per row; plus a gentle ramp that keeps P under 2^8 while
+    the reference lags behind the true max."""
+    for growth in (120.0, 6.0):
+        q, k, v, _ = random_qkv(1, 2, N, d, torch.bfloat16, 1.0, seed=91 + d + causal + int(growth))
+        q, k = ramp_keys(q, k, growth)
+        check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (0, 1)],
+                         f"4-wave small grid rising scores d={d} N={N} growth={growth}")
+
+
 def test_long_keys_full_heads_d64_causal_large_grid():
     """Causal head size 64 with 4096 keys or more on 256 workgroups or more:
     the 8-wave kernel's 128-key tiles; every row of two heads."""

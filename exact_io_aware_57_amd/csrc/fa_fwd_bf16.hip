@@ -57,8 +57,14 @@
 namespace fa {
 namespace {
 
-template <int D, int QB, int BN, int OCC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
+template <int D, int QB, int BN, int OCC, bool CAUSAL, int KS>
+__global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams p) {
+  // KS key groups of 4 waves share the workgroup's query rows: group g streams
+  // the g-th contiguous share of the key tiles through its own LDS stages, and
+  // the groups' partial results (reference max, row sum, O^T) are combined at
+  // the end, through LDS, by the same rule as a merge of split results.  With
+  // KS = 2 the longest workgroups of a causal grid take half as many steps.
+  static_assert(KS == 1 || KS == 2, "one or two key groups");
   using T = Tile<D, BN>;
   constexpr int KB = T::KB;
   constexpr int QW = 32 * QB;             // query rows per wave
@@ -68,14 +74,16 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
   // tiles 2-4% slower).
   constexpr bool kMaxFree = !(D == 64 && BN == 128);
   constexpr int BM = kWaves * QW;         // query rows per workgroup
-  // Two K/V stages as separate LDS objects, so the compiler can tell that the
-  // direct loads into one stage never alias the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char stage0[T::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[T::STAGE];
+  // Two K/V stages (per key group) as separate LDS objects, so the compiler
+  // can tell that the direct loads into one stage never alias the reads of the
+  // other.
+  __shared__ __attribute__((aligned(1024))) char stage0[KS][T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[KS][T::STAGE];
 
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);  // row wave within the key group
+  const int kgrp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);  // key group
   const int lane = tid & 63;
   const int r32 = lane & 31;
   const int hi = lane >> 5;
@@ -111,7 +119,11 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
   const int qw0 = q0 + wave * QW;
   int kv_end = kv_valid;
   if (CAUSAL) kv_end = min(kv_end, q0 + BM);
-  const int ntk = (kv_end + BN - 1) / BN;
+  // key tiles [t_begin, t_end) of this key group; every group runs nsteps steps
+  const int ntk_all = (kv_end + BN - 1) / BN;
+  const int nsteps = (ntk_all + KS - 1) / KS;
+  const int t_begin = kgrp * nsteps;
+  const int t_end = min(ntk_all, t_begin + nsteps);
 
   // ---- Q tile -> registers (B operand of S^T = K Q^T) -----------------------
   // B[k][j] for lane l: j = l % 32 (query), k = 8*(l/32) + e (head dim).
@@ -337,22 +349,75 @@ __global__ __launch_bounds__(kThreads, OCC) void fwd_bf16_kernel(FwdParams p) {
 
   // One step: start the loads of tile t+1 into `next`, compute tile t from
   // `cur`, then wait for this wave's loads and meet the other waves.
-  auto step = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
-    if (t + 1 < ntk) issue_loads(t + 1, next);
+  char* const st0 = stage0[kgrp];
+  char* const st1 = stage1[kgrp];
+  auto step = [&](int s, const char* cur, char* next) __attribute__((always_inline)) {
+    const int t = t_begin + s;
+    if (t + 1 < t_end) issue_loads(t + 1, next);
     const int k0 = t * BN;
-    const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
+    const bool active = t < t_end && (!CAUSAL || (k0 <= qw0 + QW - 1));
     if (active) tile(cur, k0);
     wait_vmem();
     __syncthreads();
   };
 
-  if (ntk > 0) issue_loads(0, stage0);
+  if (t_begin < t_end) issue_loads(t_begin, st0);
   wait_vmem();
   __syncthreads();
   // Unrolled by two so that each access names a fixed stage.
-  for (int t = 0; t < ntk; t += 2) {
-    step(t, stage0, stage1);
-    if (t + 1 < ntk) step(t + 1, stage1, stage0);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, st0, st1);
+    if (s + 1 < nsteps) step(s + 1, st1, st0);
+  }
+
+  if constexpr (KS == 2) {
+    // Key group 1 hands its (reference max, row sum, O^T) to group 0 through
+    // LDS, lane for lane (both groups hold the same rows in the same layout),
+    // a 32-column block of O^T at a time; group 0 rescales both to the larger
+    // reference and adds.  The stage buffers are free after the loop's last
+    // barrier.
+    float* xch = reinterpret_cast<float*>(&stage0[0][0]);
+    const int slot = wave * 64 + lane;
+    float wa[QB] = {}, wb[QB] = {};
+    if (kgrp == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        xch[(2 * qb) * 256 + slot] = m_run[qb];
+        xch[(2 * qb + 1) * 256 + slot] = l_run[qb];
+      }
+    }
+    __syncthreads();
+    if (kgrp == 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mb = xch[(2 * qb) * 256 + slot];
+        const float lb = xch[(2 * qb + 1) * 256 + slot];
+        const float m = fmaxf(m_run[qb], mb);
+        wa[qb] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+        wb[qb] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
+        l_run[qb] = l_run[qb] * wa[qb] + lb * wb[qb];
+        m_run[qb] = m;
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < T::DB; ++cb) {
+      __syncthreads();
+      if (kgrp == 1) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xch[(qb * 16 + r) * 256 + slot] = oacc[qb][cb][r];
+      }
+      __syncthreads();
+      if (kgrp == 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            oacc[qb][cb][r] = oacc[qb][cb][r] * wa[qb] + xch[(qb * 16 + r) * 256 + slot] * wb[qb];
+      }
+    }
+    if (kgrp != 0) return;
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ---------------------------
@@ -827,15 +892,15 @@ hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_pp_kernel<D, BN, CAUSAL>), grid, dim3(512), args, 0, stream);
 }
 
-template <int D, int QB, int BN, int OCC, bool CAUSAL>
+template <int D, int QB, int BN, int OCC, bool CAUSAL, int KS = 1>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr int BM = kWaves * 32 * QB;
   const int ntiles = (p.N + BM - 1) / BM;
   const dim3 grid((unsigned)ntiles * (unsigned)p.H * (unsigned)p.B);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, QB, BN, OCC, CAUSAL>), grid, dim3(kThreads), args, 0,
-                         stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, QB, BN, OCC, CAUSAL, KS>), grid,
+                         dim3(kThreads * KS), args, 0, stream);
 }
 
 }  // namespace
@@ -867,6 +932,14 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     // above) and 64-key tiles below, where a workgroup sees only a few tiles.
     const bool pp_long = p.causal ? (pp_groups >= 256 && p.N >= 4096) : (pp_groups >= 256 && p.N >= 2048);
     if (pp_long) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
+    // Causal grids that fit the chip in one round at two 8-wave workgroups per
+    // compute unit (at most 512 workgroups of 128 rows) split each workgroup's
+    // keys over two groups of 4 waves: the longest workgroups, which set the
+    // time of a small causal launch, take half as many steps (4-10% less time
+    // on grids of 128 to 256 such workgroups; 2-9% more on grids of 768 to 1024,
+    // which no longer fit in one round).
+    const long long w4_groups = (long long)p.B * p.H * ((p.N + 127) / 128);
+    if (p.causal && w4_groups <= 512 && !(pp && p.N >= 1024)) return launch<64, 1, 64, 2, true, 2>(p, stream);
     if (p.N >= 2048) return p.causal ? launch<64, 1, 128, 2, true>(p, stream) : launch<64, 1, 128, 2, false>(p, stream);
     if (pp && p.N >= 1024) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);

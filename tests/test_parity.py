@@ -221,7 +221,9 @@ def test_large_grid_full_heads_long_keys_d64(causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_keys_full_heads_d64_small_grid(causal):
     """Head size 64, 2048 keys or more, fewer than 256 workgroups: the 4-wave
-    kernel with 128-key tiles; ragged tail, padding and rising scores."""
+    kernel with 128-key tiles (non-causal), or with 64-key tiles and the keys
+    split over two groups of waves (causal: a padded batch leaves the second
+    group with few or no tiles); ragged tail, padding and rising scores."""
     B, H, N = 2, 4, 2100
     q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=51 + causal)
     check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (1, 3)], "4-wave 128-key tiles d=64 N=2100")

@@ -22,6 +22,11 @@ roofline     the kernel's algorithmic FLOP per launch / its average duration,
              kernel source has changed since the counters were taken.
 cpu_baseline the CPU oracle (float64 numpy, full score matrix) timed on this
              host on a bounded sample (whole heads of the same workload).
+device_reference
+             context from the same device after the timed region: the bf16 rate
+             of a plain library GEMM (torch.matmul) and the read bandwidth of a
+             plain streaming kernel, and the attention kernel's rate over that
+             GEMM rate.  Not part of the attention path.
 """
 import argparse
 import hashlib
@@ -310,6 +315,42 @@ def time_fp8(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal=True
             "frac_of_fp8_peak": round(flops / (m_kern * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
 
 
+def device_reference(dev):
+    """Context from the same device, measured after the timed region: the bf16
+    matrix rate a plain library GEMM reaches (torch.matmul, 8192^3) and the read
+    bandwidth of a plain streaming kernel (row sums over a 1 GiB float32 tensor).
+    Neither is part of the attention path; they show what the datasheet peaks
+    translate to on this machine."""
+    import torch
+
+    def timed(f, n):
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    for _ in range(20):   # clock ramp
+        a @ b
+    gemm_ms = timed(lambda: a @ b, 20)
+    del a, b
+    x = torch.ones((1 << 28) // 1024, 1024, device=dev, dtype=torch.float32)
+    read_ms = timed(lambda: x.sum(dim=1), 20)
+    del x
+    return {"bf16_gemm_tflops": round(2 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm": "torch.matmul bf16 8192x8192x8192",
+            "read_gbs": round((1 << 30) / (read_ms * 1e-3) / 1e9, 1),
+            "read": "row sums of a 1 GiB float32 tensor"}
+
+
 def cpu_baseline(index, heads):
     """The oracle as it stands on `heads` whole heads of the workload."""
     import numpy as np
@@ -589,6 +630,9 @@ def main(argv=None):
                 "kernel_ms_avg": round(ms_kernel, 5), "kernel_ms_min": round(ms_kernel_min, 5),
                 "flop_per_launch": main_p.flops, "compulsory_bytes": main_p.bytes}
 
+    ref = device_reference(dev)
+    ref["attention_over_gemm"] = round(achieved / ref["bf16_gemm_tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_heads)
@@ -610,6 +654,7 @@ def main(argv=None):
                    "key_padding": wl.padded, "input_std": wl.std, "scale": wl.scale},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "device_reference": ref,
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "other_workloads": others,
         "context_from_pages": "A100 (HBM ~1.5 TB/s, SRAM up to 19 TB/s): FlashAttention 25-40% of peak, "

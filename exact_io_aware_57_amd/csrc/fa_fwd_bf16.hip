@@ -40,8 +40,8 @@
 //    tile's max unless the tile's sum of P exceeds 2^8, which every P <= 2^8
 //    rules out (P may reach 2^8 in between); the 4-wave kernel with 128-key
 //    tiles at head size 64 instead computes each tile's max and moves the
-//    reference when the max exceeds it by more than 2^8 in the exponent.  The output is divided by the row sum once
-//    at the end.
+//    reference when the max exceeds it by more than 2^8 in the exponent.  The
+//    output is divided by the row sum once at the end.
 //  * Masks are applied only on tiles that straddle a boundary (causal diagonal,
 //    last valid key), by a branch that overwrites the score tile in place;
 //    tiles wholly above a wave's causal diagonal are skipped.

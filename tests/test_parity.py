@@ -258,6 +258,18 @@ def test_long_keys_full_heads_d64_causal_large_grid():
     check_full_heads(q, k, v, 0.125, True, None, [(0, 7)], "8-wave 128-key tiles causal d=64 N=4100 rising scores")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_very_long_single_sequence(d):
+    """One sequence of 32768 positions and two heads, causal: at head size 64 the
+    two-key-group 4-wave kernel (512 workgroups of 128 rows, up to 512 key tiles
+    each, split over the two groups), at head size 128 the 8-wave kernel on 256
+    workgroups; sampled rows, the last ones included, against the oracle."""
+    B, H, N = 1, 2, 32768
+    q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=99 + d)
+    check_sampled_rows(q, k, v, 1.0 / math.sqrt(d), True, None, [(0, 0), (0, 1)], f"single sequence N={N} d={d}",
+                       n_rows=40, seed=d)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_keys_full_heads_d128_tiny_grid(causal):
     """Head size 128 from 1024 keys up runs the 8-wave kernel on any grid, down

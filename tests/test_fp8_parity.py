@@ -141,15 +141,17 @@ def test_fp8_rising_scores(growth, causal):
     check(q8, k8, v8, (1.0, 1.0, 1.0), 0.125, causal, None, f"rising scores growth={growth}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_large_grid(causal):
+def test_fp8_large_grid(causal, d):
     """Many workgroups per head (sampled rows, every row checked for finiteness),
     and bitwise repeatable."""
-    q8, k8, v8, ds, _ = random_qkv_fp8(1, 16, 4, 4096, 128, 1.0, 23 + causal)
+    q8, k8, v8, ds, _ = random_qkv_fp8(1, 16, 4, 4096, d, 1.0, 23 + causal + d)
+    scale = 1.0 / math.sqrt(d)
     rng = np.random.default_rng(causal)
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4094, 4095], rng.integers(0, 4096, size=40)]))
-    o1, l1 = check(q8, k8, v8, ds, 0.0884, causal, None, "large grid", heads=[(0, 0), (0, 7), (0, 15)], rows=rows)
-    o2, l2 = gpu_fp8(q8, k8, v8, ds, 0.0884, causal, None)
+    o1, l1 = check(q8, k8, v8, ds, scale, causal, None, f"large grid d={d}", heads=[(0, 0), (0, 7), (0, 15)], rows=rows)
+    o2, l2 = gpu_fp8(q8, k8, v8, ds, scale, causal, None)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 

@@ -565,7 +565,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Every (batch, head, query tile) is independent, so the work would shard over GPUs by batch and head "
               "with no exchange; run with --gpus 1.", file=sys.stderr)
         return 2

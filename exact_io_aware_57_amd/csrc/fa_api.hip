@@ -14,7 +14,7 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-// Per-device verdict of the architecture check: 0 unknown, 1 gfx950, 2 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 int check_device() {

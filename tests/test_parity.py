@@ -80,12 +80,12 @@ def test_workload_parity_full(index):
                          fp32=workload(index).dtype == "fp32", tag=f"workload {index}", stated_workload=True)
 
 
-def test_workload5_sampled_rows():
+def test_long_context_sampled_rows():
     """Long-context causal d=128 at full size: sampled rows one by one, plus
     properties that hold for every row."""
     inp = make_inputs(5)
     q, k, v = inp["q"], inp["k"], inp["v"]
-    say(f"[parity] workload 5 full size {tuple(q.shape)}")
+    say(f"[parity] long context full size {tuple(q.shape)}")
     o, lse = gpu_forward(q, k, v, inp["scale"], True, None)
     og, lg = o.float().cpu(), lse.cpu()
     assert torch.isfinite(og).all() and torch.isfinite(lg).all()
@@ -102,7 +102,7 @@ def test_workload5_sampled_rows():
         total += e.sum()
         count += e.size
         worst_l = max(worst_l, np.abs(lg[0, h, rows].double().numpy() - lse_ref).max())
-    say(f"[parity] workload 5 sampled: O max {worst:.3e} mean {total / count:.3e} LSE max {worst_l:.3e}")
+    say(f"[parity] long context sampled: O max {worst:.3e} mean {total / count:.3e} LSE max {worst_l:.3e}")
     assert worst <= BF16_MAX and total / count <= BF16_MEAN and worst_l <= BF16_LSE
     # causal row 0 attends to key 0 only: O_0 = v_0 exactly, LSE_0 = scale * q0.k0
     assert torch.equal(o[0, :, 0].cpu(), v[0, :, 0])

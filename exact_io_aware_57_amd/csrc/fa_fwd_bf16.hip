@@ -33,7 +33,7 @@
 //    v_exp_f32 (base 2), half a v_cvt_pk_bf16_f32 and the row sum: in the
 //    8-wave kernel one float32 add (a tree per tile over the unrounded P; the
 //    bf16-rounded P feeds the second product, so the weights sum to 1 within
-//    the 2^-9 of that rounding), in the 4-wave kernel half a v_dot2 over the
+//    the 2^-8 of that rounding), in the 4-wave kernel half a v_dot2 over the
 //    rounded P.  v_dot2 runs on the matrix pipeline and slows several-fold
 //    next to another wave's products, which the 8-wave kernel always has.  The
 //    reference max of a row changes rarely: the kernels do not even compute a
@@ -910,7 +910,6 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   // ping-pong kernel: 256 query rows each), from same-process timings of every
   // candidate on gfx950 over grids of 32 to 2048 such workgroups.
   const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
-  const bool pp = pp_groups >= (p.causal ? 1024 : 256);
   if (p.d == 256) {
     // 32-key tiles: the score tile, the Q fragments (64 registers) and O^T (128)
     // of a wave then fit two waves per SIMD.  On grids of 256 (non-causal) and
@@ -932,22 +931,25 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     // above) and 64-key tiles below, where a workgroup sees only a few tiles.
     const bool pp_long = p.causal ? (pp_groups >= 256 && p.N >= 4096) : (pp_groups >= 256 && p.N >= 2048);
     if (pp_long) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
-    // Causal grids that fit the chip in one round at two 8-wave workgroups per
-    // compute unit (at most 512 workgroups of 128 rows) split each workgroup's
-    // keys over two groups of 4 waves: the longest workgroups, which set the
-    // time of a small causal launch, take half as many steps (4-10% less time
-    // on grids of 128 to 256 such workgroups; 2-9% more on grids of 768 to 1024,
-    // which no longer fit in one round).
+    // Below that the 4-wave kernel runs, also on full grids: under 2048 keys it
+    // takes 4-8% less time than the ping-pong kernel with 64-key tiles
+    // (non-causal) and 16-33% less (causal, 1024 and 1536 keys, 256 to 512
+    // heads).  Causal grids that fit the chip in one round at two 8-wave
+    // workgroups per compute unit (at most 512 workgroups of 128 rows) split
+    // each workgroup's keys over two groups of 4 waves: the longest
+    // workgroups, which set the time of a small causal launch, take half as
+    // many steps (4-10% less time on grids of 128 to 256 such workgroups; 2-9%
+    // more on grids of 768 to 1024, which no longer fit in one round).
     const long long w4_groups = (long long)p.B * p.H * ((p.N + 127) / 128);
-    if (p.causal && w4_groups <= 512 && !(pp && p.N >= 1024)) return launch<64, 1, 64, 2, true, 2>(p, stream);
+    if (p.causal && w4_groups <= 512) return launch<64, 1, 64, 2, true, 2>(p, stream);
     if (p.N >= 2048) return p.causal ? launch<64, 1, 128, 2, true>(p, stream) : launch<64, 1, 128, 2, false>(p, stream);
-    if (pp && p.N >= 1024) return p.causal ? launch_pp<64, 64, true>(p, stream) : launch_pp<64, 64, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }
   // Head size 128: the ping-pong kernel from 1024 keys up at any grid size
   // (4-28% less time than the 4-wave kernel on grids of 32 to 512 workgroups,
-  // causal or not), and on full grids below that.
-  if (pp || p.N >= 1024) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
+  // causal or not); below 1024 keys the 4-wave kernel, also on full grids
+  // (10-14% less time at 512 keys on 512 and 1024 heads).
+  if (p.N >= 1024) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
   return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }
 

@@ -76,7 +76,7 @@ typedef enum fa_status {
  * second product.  The row sum is taken over that rounded P in the kernels for
  * partial grids and short key ranges, and over the float32 P before rounding
  * in the 8-wave kernel for full grids and long key ranges (the weights then
- * sum to 1 within 2^-9).
+ * sum to 1 within 2^-8, the unit roundoff of bf16).
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

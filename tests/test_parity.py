@@ -1,11 +1,15 @@
 """GPU parity: the HIP path (through the C-ABI) against the float64 CPU oracle.
 
 Tolerances.  bf16 outputs: max-abs <= 1e-2 and mean-abs <= 1e-3 on O.  fp32
-path: max-abs <= 1e-5 on O and LSE.  LSE of the bf16 path: max-abs <= 2.5e-3,
+path: max-abs <= 1e-5 on O and LSE.  LSE of the bf16 path: max-abs <= 4.5e-3,
 derived from the arithmetic: LSE = ln2 * (m + log2 l) with l the sum of the
-bf16-rounded probabilities, each within a relative 2^-9 of the exact value, so
-|l/l_exact - 1| <= 2^-9 and |dLSE| <= ln(1 + 2^-9) ~ 1.95e-3, plus float32
-rounding of the sum and of m (far below 1e-4 at these sizes).
+probabilities; where they are summed after rounding to bf16 (8-bit
+significand, unit roundoff 2^-8) each is within a relative 2^-8 of the exact
+value, so |l/l_exact - 1| <= 2^-8 and |dLSE| <= ln(1 + 2^-8) ~ 3.9e-3.  The
+scores carry the float32 accumulation error of d products, at most
+d 2^-24 scale sum_c |q_c| |k_c|: up to 6e-4 on the rising-score inputs, whose
+scores reach about 110, and far below 1e-4 elsewhere, as is the float32
+rounding of the sum and of m.
 
 The five stated workloads are held to those bounds against the exact oracle.
 For the other shapes (a handful of keys per row) rounding the exact answer to
@@ -25,7 +29,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-BF16_MAX, BF16_MEAN, BF16_LSE = 1e-2, 1e-3, 2.5e-3
+BF16_MAX, BF16_MEAN, BF16_LSE = 1e-2, 1e-3, 4.5e-3
 F32_MAX, F32_LSE = 1e-5, 1e-5
 
 DEV = "cuda:0"
@@ -157,8 +161,9 @@ def check_full_heads(q, k, v, scale, causal, seqlens, heads, tag):
     Element bound 1e-2 + 2^-7 |O|: the absolute 1e-2 of the other tests covers
     rows that average many values (|O| well below 1), while rows dominated by
     one key have |O| up to max |V| (about 4 here), where rounding O to bf16
-    alone costs up to 2^-8 |O| and the bf16-rounded weights, normalised by the
-    sum of the unrounded ones, another 2^-9 |O| twice over."""
+    alone costs up to 2^-8 |O| and the bf16-rounded weights (each within 2^-8
+    of its value), normalised by the sum of the unrounded ones, another
+    2^-8 |O|."""
     say(f"[parity] {tag}: q {tuple(q.shape)} k {tuple(k.shape)} causal={causal} "
         f"seqlens={None if seqlens is None else seqlens.tolist()}")
     o, lse = gpu_forward(q, k, v, scale, causal, seqlens)
@@ -193,10 +198,11 @@ def ramp_keys(q, k, growth):
     return (q.float() + 4.0 * u).to(q.dtype), (k.float() + ramp).to(k.dtype)
 
 
-# Grids large enough for the 8-wave kernel at head size 128 (query tiles of 256
-# rows): ragged lengths, padding, scores that keep rising (the rare path that
-# moves a row's reference max and rescales its accumulators); every row of a
-# few heads checked.
+# Full grids (256 heads or more): ragged lengths, padding, scores that keep
+# rising (the rare path that moves a row's reference max and rescales its
+# accumulators); every row of a few heads checked.  Head size 64 runs the
+# 4-wave kernel at every length here, head size 128 the 4-wave kernel under
+# 1024 keys and the 8-wave kernel from there, head size 256 the 8-wave kernel.
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_ragged(d, causal):

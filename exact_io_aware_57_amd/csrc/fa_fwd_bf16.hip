@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
   // the g-th contiguous share of the key tiles through its own LDS stages, and
   // the groups' partial results (reference max, row sum, O^T) are combined at
   // the end, through LDS, by the same rule as a merge of split results.  With
-  // KS = 2 the longest workgroups of a causal grid take half as many steps.
+  // KS = 2 the longest workgroups of a causal grid take half as many steps,
+  // and a small grid keeps more waves per compute unit busy.
   static_assert(KS == 1 || KS == 2, "one or two key groups");
   using T = Tile<D, BN>;
   constexpr int KB = T::KB;
@@ -79,6 +80,9 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
   // other.
   __shared__ __attribute__((aligned(1024))) char stage0[KS][T::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[KS][T::STAGE];
+  // the merge of the key groups passes one float per accumulator register of a
+  // 32-column block of O^T through stage0
+  static_assert(KS == 1 || QB * 16 * 256 * 4 <= KS * T::STAGE, "the key-group exchange fits stage0");
 
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -934,21 +938,36 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     // Below that the 4-wave kernel runs, also on full grids: under 2048 keys it
     // takes 4-8% less time than the ping-pong kernel with 64-key tiles
     // (non-causal) and 16-33% less (causal, 1024 and 1536 keys, 256 to 512
-    // heads).  Causal grids that fit the chip in one round at two 8-wave
-    // workgroups per compute unit (at most 512 workgroups of 128 rows) split
-    // each workgroup's keys over two groups of 4 waves: the longest
-    // workgroups, which set the time of a small causal launch, take half as
-    // many steps (4-10% less time on grids of 128 to 256 such workgroups; 2-9%
-    // more on grids of 768 to 1024, which no longer fit in one round).
+    // heads).  Small grids split each workgroup's keys over two groups of 4
+    // waves, so that 128-row workgroups of 8 waves cover the chip: from 1024
+    // keys on grids of at most 256 such workgroups with 128-key tiles (one
+    // workgroup per compute unit; 11-17% less time than one key group,
+    // non-causal, and 7-9% less than two groups with 64-key tiles, causal).
+    // Causal grids up to 512 workgroups, which still fit the chip in one round
+    // at two 8-wave workgroups per compute unit, take 64-key tiles: the
+    // longest workgroups, which set the time of a small causal launch, take
+    // half as many steps (4-10% less time than one group on grids of 128 to
+    // 256 workgroups; 2-9% more on grids of 768 to 1024, which no longer fit
+    // in one round).
     const long long w4_groups = (long long)p.B * p.H * ((p.N + 127) / 128);
+    if (p.N >= 1024 && w4_groups <= 256)
+      return p.causal ? launch<64, 1, 128, 1, true, 2>(p, stream) : launch<64, 1, 128, 1, false, 2>(p, stream);
     if (p.causal && w4_groups <= 512) return launch<64, 1, 64, 2, true, 2>(p, stream);
     if (p.N >= 2048) return p.causal ? launch<64, 1, 128, 2, true>(p, stream) : launch<64, 1, 128, 2, false>(p, stream);
     return p.causal ? launch<64, 1, 64, 2, true>(p, stream) : launch<64, 1, 64, 2, false>(p, stream);
   }
-  // Head size 128: the ping-pong kernel from 1024 keys up at any grid size
-  // (4-28% less time than the 4-wave kernel on grids of 32 to 512 workgroups,
-  // causal or not); below 1024 keys the 4-wave kernel, also on full grids
-  // (10-14% less time at 512 keys on 512 and 1024 heads).
+  // Head size 128: grids of at most 128 ping-pong workgroups leave compute
+  // units idle; from 768 keys they run the 4-wave kernel with two key groups
+  // and 64-key tiles instead (128-row workgroups of 8 waves, one per compute
+  // unit: 19-27% less time than the ping-pong kernel on grids of 32 to 128,
+  // causal or not; on grids of 192 and 256 it is 10-16% faster for some causal
+  // shapes and 8-37% slower for others).  Larger grids take the ping-pong
+  // kernel from 1024 keys up (4-28% less time than the 4-wave kernel with one
+  // key group on grids of 256 to 512 workgroups) and the 4-wave kernel below
+  // (10-14% less time than the ping-pong kernel at 512 keys on 512 and 1024
+  // heads).
+  if (pp_groups <= 128 && p.N >= 768)
+    return p.causal ? launch<128, 1, 64, 1, true, 2>(p, stream) : launch<128, 1, 64, 1, false, 2>(p, stream);
   if (p.N >= 1024) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
   return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }

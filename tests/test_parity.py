@@ -144,8 +144,8 @@ def check_sampled_rows(q, k, v, scale, causal, seqlens, heads, tag, n_rows=40, s
 
 # Grids large enough for the 8-wave kernel at head size 64 (at least 256
 # workgroups of 256 rows; causal: 4096 keys or more); head size 128 takes it
-# from 1024 keys up at any grid size.  The small shapes elsewhere in this file
-# run the 4-wave kernel.
+# from 1024 keys up on grids of more than 128 such workgroups.  The small
+# shapes elsewhere in this file run the 4-wave kernel.
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_kernel(d, causal):
@@ -226,10 +226,12 @@ def test_large_grid_full_heads_long_keys_d64(causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_keys_full_heads_d64_small_grid(causal):
-    """Head size 64, 2048 keys or more, fewer than 256 workgroups: the 4-wave
-    kernel with 128-key tiles (non-causal), or with 64-key tiles and the keys
-    split over two groups of waves (causal: a padded batch leaves the second
-    group with few or no tiles); ragged tail, padding and rising scores."""
+    """Head size 64, 2048 keys or more, small grids.  Two heads of 8 (136
+    workgroups of 128 rows) run the 4-wave kernel with the keys split over two
+    groups of waves and 128-key tiles (a padded batch leaves the second group
+    with few or no tiles); 24 heads (408 workgroups) run it with one key group
+    (non-causal) or with two and 64-key tiles (causal).  Ragged tail, padding
+    and rising scores."""
     B, H, N = 2, 4, 2100
     q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=51 + causal)
     check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (1, 3)], "4-wave 128-key tiles d=64 N=2100")
@@ -237,6 +239,8 @@ def test_long_keys_full_heads_d64_small_grid(causal):
     check_full_heads(q, k, v, 0.125, causal, sl, [(0, 1), (1, 2)], "4-wave 128-key tiles d=64 N=2100 padding")
     q, k = ramp_keys(q, k, 120.0)
     check_full_heads(q, k, v, 0.125, causal, None, [(1, 0)], "4-wave 128-key tiles d=64 N=2100 rising scores")
+    q, k, v, _ = random_qkv(1, 24, N, 64, torch.bfloat16, 1.0, seed=53 + causal)
+    check_full_heads(q, k, v, 0.125, causal, None, [(0, 0), (0, 23)], "4-wave d=64 N=2100 24 heads")
 
 
 @pytest.mark.parametrize("d,N", [(64, 1000), (128, 700)])
@@ -278,15 +282,19 @@ def test_very_long_single_sequence(d):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_keys_full_heads_d128_tiny_grid(causal):
-    """Head size 128 from 1024 keys up runs the 8-wave kernel on any grid, down
-    to a few workgroups: every row of each head, ragged tails and padding."""
-    for N in (1024, 1500, 2100):
+    """Head size 128 from 768 keys on grids of at most 128 workgroups of 256
+    rows runs the 4-wave kernel with the keys split over two groups of waves
+    and 64-key tiles: every row of each head, ragged tails, padding (one row
+    block with no keys for the second group) and rising scores."""
+    for N in (768, 1024, 1500, 2100):
         q, k, v, _ = random_qkv(1, 2, N, 128, torch.bfloat16, 1.0, seed=61 + N + causal)
         check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, None, [(0, 0), (0, 1)],
-                         f"8-wave d=128 tiny grid N={N}")
+                         f"two key groups d=128 tiny grid N={N}")
+    q, k = ramp_keys(q, k, 120.0)
+    check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, None, [(0, 1)], "two key groups d=128 rising scores")
     q, k, v, _ = random_qkv(2, 1, 1500, 128, torch.bfloat16, 1.0, seed=67 + causal)
-    sl = torch.tensor([1025, 300], dtype=torch.int32)
-    check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, sl, [(0, 0), (1, 0)], "8-wave d=128 tiny grid padding")
+    sl = torch.tensor([1025, 60], dtype=torch.int32)
+    check_full_heads(q, k, v, 1.0 / math.sqrt(128), causal, sl, [(0, 0), (1, 0)], "two key groups d=128 tiny grid padding")
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -322,8 +330,9 @@ def test_grouped_query_parity(H, H_kv, d, causal):
 @pytest.mark.parametrize("d,N", [(64, 2100), (128, 1500)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_grouped_query_long_keys_small_grid(d, N, causal):
-    """Grouped heads on the paths small grids take with long key ranges: the
-    4-wave kernel's 128-key tiles (d = 64) and the 8-wave kernel (d = 128)."""
+    """Grouped heads on the path small grids take with long key ranges: the
+    4-wave kernel with two key groups (128-key tiles at d = 64, 64-key tiles at
+    d = 128)."""
     q, k, v, seqlens = random_qkv_grouped(2, 4, 2, N, d, torch.bfloat16, 1.0, seed=80 + d + causal, len_range=(N // 2, N))
     check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, seqlens, [(0, 0), (0, 3), (1, 1)],
                      f"grouped long keys small grid d={d} N={N}")

@@ -75,18 +75,29 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
+// KS key groups of 4 waves share the workgroup's 128 query rows: group g
+// streams the g-th contiguous share of the key tiles through its own LDS
+// stages, and group 1 hands its reference max, row sum and O^T to group 0 at
+// the end, which combines them as a merge of split results.  Two groups keep
+// 8 waves per compute unit busy on grids too small for two 4-wave workgroups
+// per compute unit.
+template <int D, bool CAUSAL, int KS>
+__global__ __launch_bounds__(kThreads * KS, KS == 1 ? 2 : 1) void fwd_fp8_kernel(FwdParams p) {
+  static_assert(KS == 1 || KS == 2, "one or two key groups");
   using T = Tile8<D>;
   constexpr int BN = T::BN;
   constexpr int QW = 32;
   constexpr int BM = kWaves * QW;
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * T::MAT];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * T::MAT];
+  __shared__ __attribute__((aligned(1024))) char stage0[KS][2 * T::MAT];
+  __shared__ __attribute__((aligned(1024))) char stage1[KS][2 * T::MAT];
+  // the merge passes one float per accumulator register of a 32-column block
+  // of O^T (16 per lane, 256 lanes) through stage0
+  static_assert(KS == 1 || 16 * 256 * 4 <= KS * 2 * T::MAT, "the key-group exchange fits stage0");
 
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(KS == 1 ? tid >> 6 : (tid >> 6) & 3);
+  const int kgrp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
   const int lane = tid & 63;
   const int r32 = lane & 31;
   const int hi = lane >> 5;
@@ -280,10 +291,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
     pv();
   };
 
-  auto step = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
-    if (t + 1 < ntk) issue_loads(t + 1, next);
+  if constexpr (KS == 1) {
+    // one group: the loop as written before the key split (the generic form
+    // below compiles to a different schedule that measured about 1% slower)
+    auto step1 = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
+      if (t + 1 < ntk) issue_loads(t + 1, next);
+      const int k0 = t * BN;
+      const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
+      if (active) {
+        tile(cur, k0);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    if (ntk > 0) issue_loads(0, stage0[0]);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < ntk; t += 2) {
+      step1(t, stage0[0], stage1[0]);
+      if (t + 1 < ntk) step1(t + 1, stage1[0], stage0[0]);
+    }
+  } else {
+  // Group g takes tiles [t_begin, t_end); both groups run the same number of
+  // steps, so every workgroup barrier is reached by all 8 waves.
+  const int nsteps = (ntk + KS - 1) / KS;
+  const int t_begin = kgrp * nsteps;
+  const int t_end = min(ntk, t_begin + nsteps);
+  char* const st0 = stage0[kgrp];
+  char* const st1 = stage1[kgrp];
+  auto step = [&](int s, const char* cur, char* next) __attribute__((always_inline)) {
+    const int t = t_begin + s;
+    if (t + 1 < t_end) issue_loads(t + 1, next);
     const int k0 = t * BN;
-    const bool active = !CAUSAL || (k0 <= qw0 + QW - 1);
+    const bool active = t < t_end && (!CAUSAL || (k0 <= qw0 + QW - 1));
     if (active) {
       tile(cur, k0);
     }
@@ -291,12 +331,50 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
     __syncthreads();
   };
 
-  if (ntk > 0) issue_loads(0, stage0);
+  if (t_begin < t_end) issue_loads(t_begin, st0);
   wait_vmem();
   __syncthreads();
-  for (int t = 0; t < ntk; t += 2) {
-    step(t, stage0, stage1);
-    if (t + 1 < ntk) step(t + 1, stage1, stage0);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, st0, st1);
+    if (s + 1 < nsteps) step(s + 1, st1, st0);
+  }
+  }
+
+  if constexpr (KS == 2) {
+    // The stage buffers are free after the loop's last barrier.  Both groups
+    // hold the same rows in the same lane layout, so the exchange is lane for
+    // lane; both reference maxima carry the same 2^8 factor in P.
+    float* xch = reinterpret_cast<float*>(&stage0[0][0]);
+    const int slot = wave * 64 + lane;
+    if (kgrp == 1) {
+      xch[slot] = m_run;
+      xch[256 + slot] = l_run;
+    }
+    __syncthreads();
+    float wa = 0.0f, wb = 0.0f;
+    if (kgrp == 0) {
+      const float mb = xch[slot];
+      const float lb = xch[256 + slot];
+      const float m = fmaxf(m_run, mb);
+      wa = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+      wb = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
+      l_run = l_run * wa + lb * wb;
+      m_run = m;
+    }
+#pragma unroll
+    for (int cb = 0; cb < T::DB; ++cb) {
+      __syncthreads();
+      if (kgrp == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[r * 256 + slot] = oacc[cb][r];
+      }
+      __syncthreads();
+      if (kgrp == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] = oacc[cb][r] * wa + xch[r * 256 + slot] * wb;
+      }
+    }
+    if (kgrp != 0) return;
   }
 
   // ---- epilogue: O = sv O^T / l, LSE = ln2 (m - 8 + log2 l) (both sums carry 2^8)
@@ -318,21 +396,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int KS>
 hipError_t launch8(const FwdParams& p, hipStream_t stream) {
   constexpr int BM = kWaves * 32;
   const int ntiles = (p.N + BM - 1) / BM;
   const dim3 grid((unsigned)ntiles * (unsigned)p.H * (unsigned)p.B);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel<D, CAUSAL>), grid, dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel<D, CAUSAL, KS>), grid, dim3(kThreads * KS), args,
+                         0, stream);
+}
+
+template <int D>
+hipError_t launch8_d(const FwdParams& p, hipStream_t stream) {
+  // Grids of at most 256 workgroups of 128 rows (one per compute unit) split
+  // each workgroup's keys over two groups of 4 waves, from 1024 keys.
+  const long long groups = (long long)p.B * p.H * ((p.N + 127) / 128);
+  if (groups <= 256 && p.N >= 1024) return p.causal ? launch8<D, true, 2>(p, stream) : launch8<D, false, 2>(p, stream);
+  return p.causal ? launch8<D, true, 1>(p, stream) : launch8<D, false, 1>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch8<64, true>(p, stream) : launch8<64, false>(p, stream);
-  return p.causal ? launch8<128, true>(p, stream) : launch8<128, false>(p, stream);
+  if (p.d == 64) return launch8_d<64>(p, stream);
+  return launch8_d<128>(p, stream);
 }
 
 }  // namespace fa

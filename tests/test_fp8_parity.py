@@ -143,6 +143,27 @@ def test_fp8_rising_scores(growth, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_fp8_small_grid_two_key_groups(causal, d):
+    """From 1024 keys on grids of at most 256 workgroups of 128 rows the keys of
+    each workgroup are split over two groups of waves and merged at the end:
+    every row of three heads (grouped K/V), a ragged tail, padding that leaves
+    the second group without keys in one batch, and rising scores."""
+    q8, k8, v8, ds, _ = random_qkv_fp8(2, 4, 2, 2100, d, 1.0, 31 + causal + d)
+    scale = 1.0 / math.sqrt(d)
+    check(q8, k8, v8, ds, scale, causal, None, f"two key groups d={d}", heads=[(0, 0), (1, 1), (1, 3)])
+    sl = torch.tensor([1300, 50], dtype=torch.int32)
+    check(q8, k8, v8, ds, scale, causal, sl, f"two key groups padding d={d}", heads=[(0, 2), (1, 0)])
+    g = torch.Generator().manual_seed(78 + causal + d)
+    N = 2100
+    q = torch.randn(1, 2, N, d, generator=g) * 0.5 + 1.0
+    k = torch.randn(1, 2, N, d, generator=g) * 0.5 + torch.linspace(0.0, 3.0, N)[:, None]
+    v = torch.randn(1, 2, N, d, generator=g)
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous() for x in (q, k, v))
+    check(q8, k8, v8, (1.0, 1.0, 1.0), 0.125 if d == 64 else 0.0884, causal, None, f"two key groups rising d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp8_large_grid(causal, d):
     """Many workgroups per head (sampled rows, every row checked for finiteness),
     and bitwise repeatable."""

@@ -28,6 +28,9 @@
 //  * O = sv * O^T / l rounded to bf16; LSE = ln2 (m - 8 + log2 l).
 // The workgroup is 4 waves x 32 query rows, K/V tiles of 64 keys double-
 // buffered in LDS by direct global->LDS loads, two workgroups per compute unit.
+// On small grids (at most 256 such workgroups, 1024 keys or more) a workgroup
+// has two groups of 4 waves on the same rows, each streaming half of the key
+// tiles, merged at the end by the rule for split results.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

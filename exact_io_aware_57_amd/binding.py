@@ -80,6 +80,38 @@ def _ptr(x):
     return None if x is None or x == 0 else ctypes.c_void_p(int(x))
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(name, t, shape, dtype):
+    """t must be a contiguous torch tensor of this shape and dtype."""
+    import torch
+
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor, got {type(t).__name__}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_workspace(t, need):
+    import torch
+
+    _need(isinstance(t, torch.Tensor) and t.dtype == torch.uint8 and t.dim() == 1 and t.is_contiguous(),
+          "workspace must be a contiguous 1-D uint8 tensor")
+    _need(t.numel() >= need, f"workspace must hold at least {need} bytes, got {t.numel()}")
+
+
+def _check_devices(ref, **tensors):
+    """ref must be on a GPU, and every tensor given (not None) on ref's device:
+    the kernels read and write these pointers directly."""
+    _need(ref.is_cuda, f"tensors must be on a GPU device, got {ref.device}")
+    for name, t in tensors.items():
+        if t is not None:
+            _need(t.device == ref.device, f"{name} must be on {ref.device}, got {t.device}")
+
+
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, stream):
     """C fa_fwd with integer device pointers (lse, seqlens, stream may be None)."""
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
@@ -117,11 +149,19 @@ def attention_forward_fp8(q8, k8, v8, descale, scale, causal=False, seqlens=None
     k8, v8 [B, H_kv, N, d] standing for descale[i] * value(code)."""
     import torch
 
-    if q8.dim() != 4 or k8.shape != v8.shape or k8.shape[0] != q8.shape[0] or k8.shape[2:] != q8.shape[2:]:
+    if q8.dim() != 4 or k8.dim() != 4 or k8.shape != v8.shape or k8.shape[0] != q8.shape[0] or k8.shape[2:] != q8.shape[2:]:
         raise ValueError(f"need q8 [B, H, N, d] and k8, v8 [B, H_kv, N, d], got {tuple(q8.shape)}, {tuple(k8.shape)}")
-    if not all(x.dtype == torch.uint8 and x.is_cuda and x.is_contiguous() for x in (q8, k8, v8)):
-        raise ValueError("q8, k8, v8 must be contiguous uint8 device tensors")
     B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check(name, t, t.shape, torch.uint8)
+    _need(len(descale) == 3, "descale must hold three scales (q, k, v)")
+    if out is not None:
+        _check("out", out, (B, H, N, d), torch.bfloat16)
+    if lse is not None:
+        _check("lse", lse, (B, H, N), torch.float32)
+    if seqlens is not None:
+        _check("seqlens", seqlens, (B,), torch.int32)
+    _check_devices(q8, k8=k8, v8=v8, out=out, lse=lse, seqlens=seqlens)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     if want_lse and lse is None:
@@ -156,20 +196,27 @@ def attention_backward(q, k, v, o, lse, dout, scale, causal=False, seqlens=None,
     the workspace are allocated with torch when not given."""
     import torch
 
-    if q.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
         raise ValueError(f"need q [B, H, N, d] and k, v [B, H_kv, N, d], got {tuple(q.shape)}, {tuple(k.shape)}")
-    if o.shape != q.shape or dout.shape != q.shape or lse.shape != q.shape[:3]:
-        raise ValueError("o and dout must match q, lse must be [B, H, N]")
-    if not all(x.dtype == torch.bfloat16 for x in (q, k, v, o, dout)) or lse.dtype != torch.float32:
-        raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
-    if not all(x.is_cuda and x.is_contiguous() for x in (q, k, v, o, dout, lse)):
-        raise ValueError("inputs must be contiguous device tensors")
     B, H, N, d = q.shape
     H_kv = k.shape[1]
+    bf = torch.bfloat16
+    for name, t, shape in (("q", q, q.shape), ("k", k, k.shape), ("v", v, k.shape), ("o", o, q.shape),
+                           ("dout", dout, q.shape)):
+        _check(name, t, shape, bf)
+    _check("lse", lse, (B, H, N), torch.float32)
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if t is not None:
+            _check(name, t, shape, bf)
+    if seqlens is not None:
+        _check("seqlens", seqlens, (B,), torch.int32)
+    need = fa_bwd_workspace_size(B, H, N)
+    if workspace is not None:
+        _check_workspace(workspace, need)
+    _check_devices(q, k=k, v=v, o=o, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, seqlens=seqlens, workspace=workspace)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = fa_bwd_workspace_size(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
@@ -204,17 +251,24 @@ def decode_forward(q, k, v, scale, causal=False, seqlens=None, num_splits=0, out
 
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
         raise ValueError(f"need q [B, H, Nq, d] and k, v [B, H_kv, Nk, d], got {tuple(q.shape)}, {tuple(k.shape)}")
-    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16) or not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be bfloat16 device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
     B, H, Nq, d = q.shape
     H_kv, Nk = k.shape[1], k.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, t.shape, torch.bfloat16)
+    if out is not None:
+        _check("out", out, q.shape, torch.bfloat16)
+    if lse is not None:
+        _check("lse", lse, (B, H, Nq), torch.float32)
+    if seqlens is not None:
+        _check("seqlens", seqlens, (B,), torch.int32)
+    need = fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits)
+    if workspace is not None:
+        _check_workspace(workspace, need)
+    _check_devices(q, k=k, v=v, out=out, lse=lse, seqlens=seqlens, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    need = fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
@@ -249,22 +303,20 @@ def attention_forward(q, k, v, scale, causal=False, seqlens=None, out=None, lse=
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, t.shape, q.dtype)
+    if out is not None:
+        _check("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _check("lse", lse, (B, H, N), torch.float32)
+    if seqlens is not None:
+        _check("seqlens", seqlens, (B,), torch.int32)
+    _check_devices(q, k=k, v=v, out=out, lse=lse, seqlens=seqlens)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    if seqlens is not None and (seqlens.dtype != torch.int32 or seqlens.shape != (B,) or not seqlens.is_cuda):
-        raise ValueError("seqlens must be an int32 [B] device tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     H_kv = k.shape[1]

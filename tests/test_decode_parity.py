@@ -6,8 +6,10 @@ per-batch valid lengths; query i sits at position L - Nq + i (oracle
 pairs are merged; the result must equal the softmax over all keys.
 
 Tolerances are those of the bf16 forward pass: max-abs <= 1e-2 on O, mean-abs
-<= 1e-3 against the oracle rounded to bf16, LSE max-abs <= 4.5e-3 (the
-partial results are held in float32, so the merge adds only float32 rounding).
+<= 1e-3 against the oracle rounded to bf16, LSE max-abs <= 1e-3 (each chunk
+sums its exponentials in float32 before they are rounded to bf16, and the
+partial results are held in float32, so the merge adds only float32
+rounding).
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-BF16_MAX, BF16_MEAN, BF16_LSE = 1e-2, 1e-3, 4.5e-3
+BF16_MAX, BF16_MEAN, BF16_LSE = 1e-2, 1e-3, 1e-3
 DEV = "cuda:0"
 
 
@@ -136,8 +138,8 @@ def test_decode_split_counts_agree():
     """Different key splits give the same answer to within the oracle bounds.
     They are not just float32 summation orders of one another: each chunk
     rounds its probabilities to bf16 relative to its own running max, so each
-    split count carries its own rounding of l (each LSE within ln(1 + 2^-8) of
-    the exact one); two split counts therefore agree within twice the bounds."""
+    split count rounds the weights applied to V differently; two split counts
+    therefore agree within twice the bounds."""
     q, k, v, sl = random_decode(2, 16, 4, 2, 4096, 128, seed=9, len_range=(3000, 4096))
     outs = [gpu_decode(q, k, v, 128 ** -0.5, False, sl, num_splits=s) for s in (1, 4, 16, 64)]
     o0, l0 = np64(outs[0][0]), np64(outs[0][1])
@@ -193,8 +195,15 @@ def test_decode_rejects_small_workspace_on_device():
     q, k, v, _ = random_decode(1, 4, 4, 1, 1000, 64, seed=15)
     need = binding.fa_decode_workspace_size(1, 4, 4, 1, 1000, 64, 0)
     ws = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
-    with pytest.raises(binding.FaError):
-        binding.decode_forward(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, False, None, workspace=ws)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    # the torch wrapper refuses it before the call ...
+    with pytest.raises(ValueError, match="workspace"):
+        binding.decode_forward(qd, kd, vd, 0.125, False, None, workspace=ws)
+    # ... and so does the C entry point itself, given the short size
+    o = torch.empty_like(qd)
+    st = binding.fa_decode(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), None, 1, 4, 4, 1, 1000, 64, 0.125,
+                           False, None, 0, ws.data_ptr(), need - 4, None)
+    assert st == binding.FA_ERR_INVALID_ARG
 
 
 def test_decode_bench_configuration():

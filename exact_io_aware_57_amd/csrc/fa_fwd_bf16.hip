@@ -34,8 +34,10 @@
 //    8-wave kernel one float32 add (a tree per tile over the unrounded P; the
 //    bf16-rounded P feeds the second product, so the weights sum to 1 within
 //    the 2^-8 of that rounding), in the 4-wave kernel half a v_dot2 over the
-//    rounded P.  v_dot2 runs on the matrix pipeline and slows several-fold
-//    next to another wave's products, which the 8-wave kernel always has.  The
+//    rounded P, which normalises O, plus one float32 add over the unrounded P,
+//    which gives the LSE.  v_dot2 runs on the matrix pipeline and slows
+//    several-fold next to another wave's products, which the 8-wave kernel
+//    always has.  The
 //    reference max of a row changes rarely: the kernels do not even compute a
 //    tile's max unless the tile's sum of P exceeds 2^8, which every P <= 2^8
 //    rules out (P may reach 2^8 in between); the 4-wave kernel with 128-key
@@ -186,11 +188,15 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
 
   // ---- running state ------------------------------------------------------------
   f32x16 oacc[QB][T::DB];
-  float m_run[QB], l_run[QB];
+  // Two row sums: l_run over the bf16-rounded P that the second product uses
+  // (the normaliser of O, so that the weights applied to V sum to one), and
+  // le_run over the float32 P before rounding (the LSE output).
+  float m_run[QB], l_run[QB], le_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.0f;
+    le_run[qb] = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < T::DB; ++cb) oacc[qb][cb] = f32x16{};
   }
@@ -249,8 +255,8 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
         // whenever the tile's sum of p is; the max is computed, and the tile
         // redone against it, only when the sum is larger, not a number, or the
         // row has no reference yet.
-        auto exps = [&](float mref) __attribute__((always_inline)) {
-          float ts = 0.0f;
+        auto exps = [&](float mref, float& te) __attribute__((always_inline)) {
+          float ts = 0.0f, te0 = 0.0f, te1 = 0.0f;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -259,11 +265,15 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
               const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
               const uint32_t pp = pack_bf16(p0, p1);
               ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, ts, false);
+              te0 += p0;
+              te1 += p1;
               pk[qb][kb][j] = pp;
             }
+          te = te0 + te1;
           return ts;
         };
-        float ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]);
+        float le;
+        float ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb], le);
         const bool bad = !(ls <= kMaxTileSum) || m_run[qb] == -INFINITY;
         if (__builtin_amdgcn_ballot_w64(bad) != 0) {
           keep_branch();
@@ -276,11 +286,13 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
           const float m_new = fmaxf(m_run[qb], mx * sc);
           alpha[qb] = (m_run[qb] == -INFINITY || m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
           l_run[qb] *= alpha[qb];
+          le_run[qb] *= alpha[qb];
           m_run[qb] = m_new;
           rescale = true;
-          ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb]);
+          ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb], le);
         }
         l_run[qb] += ls;
+        le_run[qb] += le;
         continue;
       }
       float mx = -INFINITY;
@@ -295,10 +307,12 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
         const float m_new = need ? tmax : m_run[qb];
         alpha[qb] = (m_new == m_run[qb]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         l_run[qb] *= alpha[qb];
+        le_run[qb] *= alpha[qb];
         m_run[qb] = m_new;
         rescale = true;
       }
       const float mref = (mask && m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+      float te0 = 0.0f, te1 = 0.0f;
       // this kernel keeps the row sum on v_dot2 over the packed P (measured
       // faster here than float32 adds, unlike the 8-wave kernel)
 #pragma unroll
@@ -309,8 +323,11 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
           const uint32_t pp = pack_bf16(p0, p1);
           l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run[qb], false);
+          te0 += p0;
+          te1 += p1;
           pk[qb][kb][j] = pp;
         }
+      le_run[qb] += te0 + te1;
     }
 
     // O^T = alpha O^T + V^T P^T.  MFMA (kb, u) takes accumulator registers
@@ -386,20 +403,23 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
     if (kgrp == 1) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        xch[(2 * qb) * 256 + slot] = m_run[qb];
-        xch[(2 * qb + 1) * 256 + slot] = l_run[qb];
+        xch[(3 * qb) * 256 + slot] = m_run[qb];
+        xch[(3 * qb + 1) * 256 + slot] = l_run[qb];
+        xch[(3 * qb + 2) * 256 + slot] = le_run[qb];
       }
     }
     __syncthreads();
     if (kgrp == 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float mb = xch[(2 * qb) * 256 + slot];
-        const float lb = xch[(2 * qb + 1) * 256 + slot];
+        const float mb = xch[(3 * qb) * 256 + slot];
+        const float lb = xch[(3 * qb + 1) * 256 + slot];
+        const float leb = xch[(3 * qb + 2) * 256 + slot];
         const float m = fmaxf(m_run[qb], mb);
         wa[qb] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[qb] - m);
         wb[qb] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
         l_run[qb] = l_run[qb] * wa[qb] + lb * wb[qb];
+        le_run[qb] = le_run[qb] * wa[qb] + leb * wb[qb];
         m_run[qb] = m;
       }
     }
@@ -428,6 +448,7 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = pair_sum(l_run[qb]);
+    const float le = pair_sum(le_run[qb]);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     const int qi = qw0 + qb * 32 + r32;
     if (qi < N) {
@@ -442,7 +463,7 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
           *reinterpret_cast<u32x2*>(orow + col) = w;
         }
       if (p.lse && hi == 0) {
-        p.lse[(size_t)bh * N + qi] = l > 0.0f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+        p.lse[(size_t)bh * N + qi] = le > 0.0f ? (m_run[qb] + log2f(le)) * kLn2 : -INFINITY;
       }
     }
   }

@@ -26,8 +26,10 @@
 //    a fixed number of products ahead of their use, so that they are in flight
 //    under the matrix work without holding a whole tile's operands in
 //    registers.
-//  * Softmax per score: one FMA, one v_exp_f32 (base 2), half a pack to bf16
-//    and half a v_dot2 for the row sum of the rounded P; the reference max of a
+//  * Softmax per score: one FMA, one v_exp_f32 (base 2), half a pack to bf16,
+//    half a v_dot2 for the row sum of the rounded P (the normaliser of O) and
+//    one float32 add for the row sum of the unrounded P (the LSE output); the
+//    reference max of a
 //    row moves only when a tile's max exceeds it by more than 2^8 in the
 //    exponent.  Masks only on tiles that straddle the causal diagonal or the
 //    last valid key; tiles above a wave's diagonal are skipped.
@@ -138,7 +140,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d256_kernel(FwdParams p)
   f32x16 oacc[DB];
 #pragma unroll
   for (int cb = 0; cb < DB; ++cb) oacc[cb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  // l_run sums the bf16-rounded P (the normaliser of O), le_run the float32 P
+  // before rounding (the LSE output).
+  float m_run = -INFINITY, l_run = 0.0f, le_run = 0.0f;
   const float sc = p.scale * kLog2e;
   bf16x2 ones;
   ones[0] = (__bf16)1.0f;
@@ -194,11 +198,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d256_kernel(FwdParams p)
       const float m_new = need ? tmax : m_run;
       alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
+      le_run *= alpha;
       m_run = m_new;
       rescale = true;
     }
     const float mref = (MASK && m_run == -INFINITY) ? 0.0f : m_run;
     uint32_t pk[KB][8];
+    float te0 = 0.0f, te1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -207,8 +213,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d256_kernel(FwdParams p)
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][2 * j + 1], sc, -mref));
         const uint32_t pp = pack_bf16(p0, p1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, l_run, false);
+        te0 += p0;
+        te1 += p1;
         pk[kb][j] = pp;
       }
+    le_run += te0 + te1;
 
     // ---- O^T = alpha O^T + V^T P^T: product i is row block i % DB, half u of
     // key block kb (keys 32 kb + 16 u + {0..3, 8..11} + 4 hi) ----
@@ -276,6 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d256_kernel(FwdParams p)
 
   // ---- epilogue: O = O^T / l, LSE = ln2 (m + log2 l) ----
   const float l = pair_sum(l_run);
+  const float le = pair_sum(le_run);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const int qi = qw0 + r32;
   if (qi < N) {
@@ -290,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d256_kernel(FwdParams p)
         *reinterpret_cast<u32x2*>(orow + col) = w;
         __builtin_amdgcn_sched_barrier(0);
       }
-    if (p.lse && hi == 0) p.lse[(size_t)bh * N + qi] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    if (p.lse && hi == 0) p.lse[(size_t)bh * N + qi] = le > 0.0f ? (m_run + log2f(le)) * kLn2 : -INFINITY;
   }
 }
 

@@ -105,10 +105,15 @@ def test_rows_match_full():
 
 def test_bf16_inputs_are_read_exactly():
     q, k, v, _ = random_qkv(1, 1, 16, 64, torch.bfloat16, 1.0, seed=3)
-    qf = q.float().double().numpy()
-    # every bf16 value has at most 8 significant bits, so it is exact in float64
-    assert np.all(qf == np.round(qf * 2.0 ** 20) / 2.0 ** 20) or True
-    o, lse = attention(qf, k.float().double().numpy(), v.float().double().numpy(), 0.125)
+    for t in (q, k, v):
+        x = t.float().double().numpy()
+        # float64 holds every bf16 value exactly: converting back gives the same bits
+        assert torch.equal(torch.from_numpy(x).to(torch.bfloat16), t)
+        # and each has at most 8 significant bits: mantissa * 2^8 is an integer
+        m, _ = np.frexp(x)
+        assert np.all(m * 2.0 ** 8 == np.round(m * 2.0 ** 8))
+    qf, kf, vf = (t.float().double().numpy() for t in (q, k, v))
+    o, lse = attention(qf, kf, vf, 0.125)
     assert o.dtype == np.float64 and np.isfinite(o).all() and np.isfinite(lse).all()
 
 

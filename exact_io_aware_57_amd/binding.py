@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the attention forward pass runs in the
 HIP kernels of libfa_mi355x.so.  ``fa_fwd``, ``fa_fwd_f32`` and
-``fa_fwd_gqa``, ``fa_fwd_gqa_f32``, ``fa_decode``, ``fa_decode_workspace_size`` and ``fa_status_str`` mirror
+``fa_fwd_gqa``, ``fa_fwd_gqa_f32``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_decode``,
+``fa_decode_noalloc``, ``fa_decode_workspace_size`` and ``fa_status_str`` mirror
 the C entry points one to one (raw device pointers as
 ints, a hipStream_t as an int or None).  ``attention_forward`` is a convenience
 wrapper for torch device tensors: it checks shapes, dtypes and layout, takes
@@ -21,9 +22,11 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_NO_DEVICE = -4
 FA_ERR_LAUNCH = -5
+FA_ERR_SCRATCH_TOO_SMALL = -6
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
-EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
-                    "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_noalloc", "fa_decode_workspace_size",
+                    "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -68,6 +71,8 @@ def load():
         lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp, ctypes.c_size_t, vp]
         lib.fa_decode.restype = i32
+        lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, i32, vp]
+        lib.fa_decode_noalloc.restype = i32
         lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_status_str.argtypes = [i32]
@@ -235,6 +240,14 @@ def fa_decode(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, nu
     return load().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(Nq), int(Nk),
                             int(d), float(scale), int(bool(causal)), _ptr(seqlens), int(num_splits), _ptr(workspace),
                             int(workspace_size), _ptr(stream))
+
+
+def fa_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, stream):
+    """C fa_decode_noalloc with integer device pointers (no workspace: the
+    library's static per-GPU scratch holds the partial results)."""
+    return load().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(H_kv), int(Nq),
+                                    int(Nk), int(d), float(scale), int(bool(causal)), _ptr(seqlens), int(num_splits),
+                                    _ptr(stream))
 
 
 def fa_decode_workspace_size(B, H, H_kv, Nq, Nk, d, num_splits=0):

@@ -7,9 +7,19 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_internal.h"
+
+// Static scratch of fa_decode_noalloc: the split kernel's partial results live
+// here instead of in a caller workspace.  Each GPU the library runs on holds its
+// own copy of this array (FA_DECODE_NOALLOC_SCRATCH_BYTES) until the process
+// ends, and every fa_decode_noalloc call on that GPU uses it (calls that overlap
+// on one GPU race).  Host code never passes the array's name to a kernel: on
+// the host it only stands in for the symbol, and the device address of the
+// current GPU's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -38,6 +48,30 @@ int check_device() {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Device address of each GPU's copy of `scratch` (above), looked up once per
+// device with that device current.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, or null if the lookup
+// failed.  dev is the current device (check_device() has accepted it).
+void* scratch_address(int dev) {
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    void* found = nullptr;
+    if (hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)) != hipSuccess || !found) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr = found;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 int validate(const fa::FwdParams& p) {
   if (!p.q || !p.k || !p.v || !p.o) return FA_ERR_INVALID_ARG;
@@ -97,6 +131,51 @@ int bwd_npad(int N) {
 
 size_t bwd_workspace_bytes(int B, int H, int N) { return 2 * (size_t)B * H * (size_t)bwd_npad(N) * sizeof(float); }
 
+// Validation and launch of one decode step.  ws == nullptr means the static
+// scratch (fa_decode_noalloc): the problem must then fit its fixed size.
+int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int Nq,
+                       int Nk, int d, float scale, int causal, const int32_t* seqlens, int num_splits, void* ws,
+                       size_t ws_size, void* stream) {
+  const bool use_scratch = ws == nullptr;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || num_splits < 0)
+    return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * H * Nq * d > (uint64_t(1) << 40) || (uint64_t)B * H_kv * Nk * d > (uint64_t(1) << 40))
+    return FA_ERR_INVALID_ARG;
+  const int S = decode_splits(B, H, H_kv, Nq, Nk, num_splits);
+  const long long rows = (long long)(H / H_kv) * Nq;
+  const long long qblk = (rows + fa::decode_rows_per_block() - 1) / fa::decode_rows_per_block();
+  if ((long long)B * H_kv * qblk * S > INT32_MAX || (long long)B * H * Nq > INT32_MAX) return FA_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes(B, H, Nq, d, S);
+  if (use_scratch) {
+    if (need > (size_t)FA_DECODE_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH_TOO_SMALL;
+  } else if (ws_size < need) {
+    return FA_ERR_INVALID_ARG;
+  }
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (ws && !aligned(ws, 16)))
+    return FA_ERR_MISALIGNED;
+  if (lse && !aligned(lse, 4)) return FA_ERR_MISALIGNED;
+  if (seqlens && !aligned(seqlens, 4)) return FA_ERR_MISALIGNED;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  if (use_scratch) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipGetLastError();
+      return FA_ERR_NO_DEVICE;
+    }
+    ws = scratch_address(dev);
+    if (!ws) return FA_ERR_NO_DEVICE;
+  }
+  const size_t orows = (size_t)B * H * Nq;
+  float* opart = reinterpret_cast<float*>(ws);
+  float* lpart = opart + orows * (size_t)S * (size_t)d;
+  fa::DecodeParams p{q, k, v, o, lse, seqlens, opart, lpart, B, H, H_kv, Nq, Nk, d, scale, causal ? 1 : 0, S, (int)qblk};
+  return fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,31 +219,16 @@ size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, i
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
               const int32_t* seqlens, int num_splits, void* workspace, size_t workspace_size, void* stream) {
-  if (!q || !k || !v || !o || !workspace) return FA_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || num_splits < 0)
-    return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if ((uint64_t)B * H * Nq * d > (uint64_t(1) << 40) || (uint64_t)B * H_kv * Nk * d > (uint64_t(1) << 40))
-    return FA_ERR_INVALID_ARG;
-  const int S = decode_splits(B, H, H_kv, Nq, Nk, num_splits);
-  const long long rows = (long long)(H / H_kv) * Nq;
-  const long long qblk = (rows + fa::decode_rows_per_block() - 1) / fa::decode_rows_per_block();
-  if ((long long)B * H_kv * qblk * S > INT32_MAX || (long long)B * H * Nq > INT32_MAX) return FA_ERR_INVALID_ARG;
-  if (workspace_size < workspace_bytes(B, H, Nq, d, S)) return FA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 16))
-    return FA_ERR_MISALIGNED;
-  if (lse && !aligned(lse, 4)) return FA_ERR_MISALIGNED;
-  if (seqlens && !aligned(seqlens, 4)) return FA_ERR_MISALIGNED;
-  const int st = check_device();
-  if (st != FA_OK) return st;
-  const size_t orows = (size_t)B * H * Nq;
-  float* opart = reinterpret_cast<float*>(workspace);
-  float* lpart = opart + orows * (size_t)S * (size_t)d;
-  fa::DecodeParams p{q, k, v, o, lse, seqlens, opart, lpart, B, H, H_kv, Nq, Nk, d, scale, causal ? 1 : 0, S, (int)qblk};
-  return fa::launch_decode(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  if (!workspace) return FA_ERR_INVALID_ARG;
+  return decode_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, workspace,
+                     workspace_size, stream);
 }
 
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                      const int32_t* seqlens, int num_splits, void* stream) {
+  return decode_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, nullptr, 0, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal,
@@ -219,6 +283,10 @@ const char* fa_status_str(int status) {
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte alignment, lse/seqlens 4-byte";
     case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no current HIP device";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";
+    case FA_ERR_SCRATCH_TOO_SMALL:
+      return "FA_ERR_SCRATCH_TOO_SMALL: the decode step needs more partial-result memory than the static scratch of "
+             "fa_decode_noalloc holds (FA_DECODE_NOALLOC_SCRATCH_BYTES); use fa_decode with a workspace, or fewer "
+             "splits or rows per call";
     default: return "unknown fa_status";
   }
 }

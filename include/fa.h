@@ -30,7 +30,8 @@
  *
  * Ownership and execution.  The caller owns every buffer.  The library
  * allocates no device or host memory and keeps no state across calls besides a
- * cache of device properties.  A call validates its arguments on the host,
+ * cache of device properties (and, for fa_decode_noalloc only, one static
+ * device array per GPU, described there).  A call validates its arguments on the host,
  * enqueues one kernel on `stream` (a hipStream_t; NULL = the default stream)
  * and returns without synchronising.  Calls are thread-safe.
  *
@@ -57,7 +58,8 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = -2, /* d not supported by the entry point, or the current device is not gfx950 */
   FA_ERR_MISALIGNED = -3,  /* q, k, v, o not 16-byte aligned, or lse / seqlens not 4-byte aligned */
   FA_ERR_NO_DEVICE = -4,   /* no HIP device is present or current */
-  FA_ERR_LAUNCH = -5       /* the HIP runtime refused the kernel launch */
+  FA_ERR_LAUNCH = -5,      /* the HIP runtime refused the kernel launch */
+  FA_ERR_SCRATCH_TOO_SMALL = -6 /* fa_decode_noalloc: the partial results exceed its static scratch */
 } fa_status;
 
 /*
@@ -139,6 +141,31 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* Bytes of workspace fa_decode needs for these arguments (0 for invalid ones). */
 size_t fa_decode_workspace_size(int B, int H, int H_kv, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * fa_decode without a workspace, for callers that cannot allocate device memory
+ * around the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, arithmetic and results are those of
+ * fa_decode (same kernels, same key splits); the partial results go to a static
+ * device array of FA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing and frees
+ * nothing.
+ *   Limit: fa_decode_workspace_size(...) of the same arguments must not exceed
+ *   FA_DECODE_NOALLOC_SCRATCH_BYTES, else FA_ERR_SCRATCH_TOO_SMALL is returned
+ *   and nothing is enqueued (the bench decode step, B=8 H=32 Nq=1 d=128 with 8
+ *   key splits, needs about 1 MiB).
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls that
+ *   overlap on one GPU (different streams or threads without ordering between
+ *   them) race and must not be issued; calls ordered on one stream are safe.
+ *   The array's previous contents never matter: every partial result a call
+ *   reads, it has written.
+ *   The first call on a device looks up that device's array address (once,
+ *   with that device current).
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
+                      const int32_t* seqlens, int num_splits, void* stream);
 
 /*
  * FP8 forward pass: Q, K, V as e4m3 codes with one scale per tensor.

@@ -30,8 +30,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
-                                    "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_noalloc",
+                                    "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa",
+                                    "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -52,7 +53,7 @@ def test_library_is_built_for_gfx950():
 
 def test_status_strings(lib):
     for code in (binding.FA_OK, binding.FA_ERR_INVALID_ARG, binding.FA_ERR_UNSUPPORTED, binding.FA_ERR_MISALIGNED,
-                 binding.FA_ERR_NO_DEVICE, binding.FA_ERR_LAUNCH):
+                 binding.FA_ERR_NO_DEVICE, binding.FA_ERR_LAUNCH, binding.FA_ERR_SCRATCH_TOO_SMALL):
         s = binding.fa_status_str(code)
         assert s and s != "unknown fa_status"
     assert binding.fa_status_str(12345) == "unknown fa_status"
@@ -235,3 +236,26 @@ def test_fp8_arguments_are_checked_on_the_host(lib):
         assert call_fp8(**{name: FAKE + 8}) == E.FA_ERR_MISALIGNED, name
     assert call_fp8(lse=FAKE + 2) == E.FA_ERR_MISALIGNED
     assert call_fp8() == E.FA_ERR_NO_DEVICE
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    """fa_decode_noalloc refuses, on the host, a step whose partial results
+    exceed its static scratch, and otherwise checks its arguments as fa_decode
+    does (no call here reaches a launch: the pointers are fake)."""
+    E = binding
+    scratch = E.FA_DECODE_NOALLOC_SCRATCH_BYTES
+    assert scratch == 16 << 20
+    # 4096 query rows x 8 splits x (128 + 1) floats = 16.9 MB > 16 MiB
+    big = (64, 64, 8, 1, 32768, 128)
+    assert E.fa_decode_workspace_size(*big, 8) > scratch
+    assert E.fa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, *big, 0.088, 1, None, 8, None) == E.FA_ERR_SCRATCH_TOO_SMALL
+    # the same rows with 4 splits fit; on this host the call then stops at the device check
+    assert E.fa_decode_workspace_size(*big, 4) <= scratch
+    assert E.fa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, *big, 0.088, 1, None, 4, None) in (E.FA_ERR_NO_DEVICE,
+                                                                                                 E.FA_ERR_UNSUPPORTED)
+    assert E.fa_decode_noalloc(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 64, 0.125, 0, None, 0, None) == \
+        E.FA_ERR_INVALID_ARG
+    assert E.fa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 96, 0.125, 0, None, 0, None) == \
+        E.FA_ERR_UNSUPPORTED
+    assert E.fa_decode_noalloc(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 64, 0.125, 0, None, 0, None) == \
+        E.FA_ERR_MISALIGNED

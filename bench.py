@@ -15,7 +15,12 @@ value        algorithmic TFLOP/s of the whole step: 4*d FLOP per allowed
 roofline     the kernel's algorithmic FLOP per launch / its average duration,
              from HIP events recorded on the launch stream around every timed
              launch, against the bf16 dense matrix peak of MI355X
-             (256 CU x 2.4 GHz x 4096 FLOP/clk = 2516.6 TFLOP/s).
+             (256 CU x 2.4 GHz x 4096 FLOP/clk = 2516.6 TFLOP/s).  After the
+             timed region: ``kernel_stats`` (mean, median and min over at least
+             100 launches and 200 ms), ``cold_cache`` (a 512 MiB buffer, more
+             than the 256 MB last-level cache, overwritten before each launch)
+             and ``clock`` (the graphics clock amdsmi reports while the kernel
+             runs back to back, with the matrix peak at that clock).
              ``traffic`` is the HBM bytes per launch from a committed rocprofv3
              counter summary (FETCH_SIZE and WRITE_SIZE, scaled by the same
              counters on a copy of known size); null when missing or when the
@@ -185,6 +190,116 @@ def time_launches(launch, steps, warmup):
     t1 = time.perf_counter()
     per_launch = [s.elapsed_time(e) for s, e in events]
     return (t1 - t0) * 1e3 / steps, sum(per_launch) / len(per_launch), min(per_launch)
+
+
+def kernel_stats(launch, min_launches=100, min_ms=200.0, max_launches=20000):
+    """Per-launch kernel durations (HIP events on the launch stream around each
+    launch), repeated until at least ``min_launches`` launches and ``min_ms`` of
+    kernel time: mean, median and min in ms, and the launch count."""
+    import torch
+
+    times = []
+    while len(times) < min_launches or sum(times) < min_ms:
+        n = max(10, min(min_launches, max_launches - len(times)))
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for s, e in events:
+            s.record()
+            launch()
+            e.record()
+        torch.cuda.synchronize()
+        times += [s.elapsed_time(e) for s, e in events]
+        if len(times) >= max_launches:
+            break
+    srt = sorted(times)
+    return {"launches": len(times), "mean": sum(times) / len(times), "median": srt[len(srt) // 2], "min": srt[0]}
+
+
+def cold_kernel_stats(launch, dev, launches=20, flush_mib=512):
+    """Kernel durations with the caches cold: before each launch a 512 MiB buffer
+    (more than the 256 MB last-level cache) is overwritten, so the inputs come
+    from HBM.  Events bracket the attention launch only."""
+    import torch
+
+    junk = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(launches):
+        junk.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        launch()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    del junk
+    srt = sorted(times)
+    return {"launches": launches, "mean": sum(times) / len(times), "median": srt[len(srt) // 2], "min": srt[0],
+            "flush_mib": flush_mib}
+
+
+def sample_gfx_clock(launch, kernel_ms, seconds=0.6, period_s=0.004):
+    """Graphics clock while the kernel runs back to back: amdsmi's gpu_metrics
+    (current_gfxclks, MHz per XCD, averaged over the XCDs) sampled from a host
+    thread every few ms over about ``seconds`` of launches; the first 20% of the
+    samples (clock ramp) are dropped.  Returns (median MHz, sample count) or
+    (None, 0) if the metrics are not readable."""
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if not handles:
+            return None, 0
+        handle = handles[0]
+    except Exception:
+        return None, 0
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        vals = m.get("current_gfxclks")
+        if isinstance(vals, (list, tuple)):
+            vals = [float(v) for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                v = read()
+            except Exception:
+                v = None
+            if v is not None:
+                samples.append(v)
+            time.sleep(period_s)
+
+    n = max(20, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
+    th = threading.Thread(target=sampler, daemon=True)
+    done = torch.cuda.Event()
+    th.start()
+    try:
+        for _ in range(n):
+            launch()
+        done.record()
+        while not done.query():
+            time.sleep(0.002)
+    finally:
+        stop.set()
+        th.join()
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+    keep = sorted(samples[len(samples) // 5:])
+    if not keep:
+        return None, 0
+    return keep[len(keep) // 2], len(keep)
 
 
 def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=True, std=0.5, seed=6, steps=20,
@@ -382,9 +497,19 @@ def cpu_baseline(index, heads):
     except Exception:  # pragma: no cover - informational only
         threads = None
     cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores, "kind": "oracle",
             "sample": f"{heads} whole head(s) of {wl.name} (B=1 slice, all {wl.N} query rows, float64 numpy, "
-                      f"full score matrix), {dt:.2f} s, {flops / 1e9:.1f} GFLOP algorithmic; host cores visible: {cores}"}
+                      f"full score matrix), {dt:.2f} s, {flops / 1e9:.1f} GFLOP algorithmic; host cores visible: {cores}",
+            "cpu_model": model, "blas_threads": threads, "host_cores_visible": cores,
+            "threads_note": "products run on the BLAS threads; the elementwise softmax on one thread"}
 
 
 def summarize_traffic(fetch_csv, write_csv, workload_name, command):
@@ -585,6 +710,10 @@ def main(argv=None):
     ms_step, ms_kernel, ms_kernel_min = time_launches(launch, args.steps, args.warmup)
     value = main_p.flops / (ms_step * 1e-3) / 1e12
     achieved = main_p.flops / (ms_kernel * 1e-3) / 1e12
+    # after the timed region: longer statistics, the clock, and the cold-cache variant
+    stats = kernel_stats(launch)
+    clock_mhz, clock_samples = sample_gfx_clock(launch, ms_kernel)
+    cold = cold_kernel_stats(launch, dev)
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -629,6 +758,20 @@ def main(argv=None):
                 "traffic": None if traffic is None else int(traffic["bytes"]),
                 "kernel_ms_avg": round(ms_kernel, 5), "kernel_ms_min": round(ms_kernel_min, 5),
                 "flop_per_launch": main_p.flops, "compulsory_bytes": main_p.bytes}
+    tf = lambda ms: main_p.flops / (ms * 1e-3) / 1e12  # noqa: E731
+    roofline["kernel_stats"] = {"launches": stats["launches"], "ms_mean": round(stats["mean"], 5),
+                                "ms_median": round(stats["median"], 5), "ms_min": round(stats["min"], 5),
+                                "frac_median": round(tf(stats["median"]) / PEAK_BF16_TFLOPS, 4)}
+    roofline["cold_cache"] = {"launches": cold["launches"], "flush_mib": cold["flush_mib"],
+                              "ms_median": round(cold["median"], 5), "ms_min": round(cold["min"], 5),
+                              "frac_median": round(tf(cold["median"]) / PEAK_BF16_TFLOPS, 4)}
+    if clock_mhz is not None:
+        peak_clk = 256 * 4096 * clock_mhz * 1e6 / 1e12
+        roofline["clock"] = {"gfx_mhz_median": round(clock_mhz, 1), "samples": clock_samples,
+                             "source": "amdsmi gpu_metrics current_gfxclks during back-to-back launches",
+                             "peak_at_clock": round(peak_clk, 1), "frac_at_clock": round(achieved / peak_clk, 4)}
+    else:
+        roofline["clock"] = None
 
     ref = device_reference(dev)
     ref["attention_over_gemm"] = round(achieved / ref["bf16_gemm_tflops"], 4)

@@ -24,8 +24,10 @@ static __device__ __align__(256) char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr int kMaxDevices = 64;
-// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other;
+// and the device's compute-unit count (filled by the same check).
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_num_cu[kMaxDevices];
 
 int check_device() {
   int dev = -1;
@@ -34,7 +36,7 @@ int check_device() {
     return FA_ERR_NO_DEVICE;
   }
   if (dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
-  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  int v = g_arch_ok[dev].load(std::memory_order_acquire);
   if (v == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -42,9 +44,21 @@ int check_device() {
       return FA_ERR_NO_DEVICE;
     }
     v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+    g_num_cu[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_arch_ok[dev].store(v, std::memory_order_release);
   }
   return v == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+// Compute units of the current device (after check_device() accepted it).
+int current_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  const int n = g_num_cu[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 256;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -90,11 +104,12 @@ int validate(const fa::FwdParams& p) {
   return FA_OK;
 }
 
-int run(const fa::FwdParams& p, void* stream, bool bf16) {
+int run(fa::FwdParams p, void* stream, bool bf16) {
   int st = validate(p);
   if (st != FA_OK) return st;
   st = check_device();
   if (st != FA_OK) return st;
+  p.num_cu = current_cus();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = !bf16 ? fa::launch_fwd_f32(p, s) : fa::launch_fwd_bf16(p, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -269,6 +284,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     if (!std::isfinite(s) || !(s > 0.0f)) return FA_ERR_INVALID_ARG;
   st = check_device();
   if (st != FA_OK) return st;
+  p.num_cu = current_cus();
   return fa::launch_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -102,6 +102,45 @@ __host__ __device__ __forceinline__ void pin(const V& v) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup -> (batch * head, query tile) for a grid of ntiles query tiles per
+// head and bh_count heads.
+// Without the causal mask every tile costs the same.  The dispatcher hands
+// workgroup i to XCD i % 8; XCD x gets the contiguous logical range
+// [x * per, (x + 1) * per), so neighbouring query tiles of one head share that
+// XCD's L2 for their K/V reads.
+// With the causal mask query tile qt costs about qt + 1 key tiles.  On a grid
+// of at most four rounds of ncu workgroups (ncu compute units) the whole grid
+// is resident at once, and the hardware places workgroups i, i + ncu, i + 2 ncu,
+// ... on one compute unit (measured on gfx950), so the logical order decides
+// how much work each unit gets: tiles are ranked heaviest first (query tile
+// descending, then head), and odd rounds take their ranks in reverse order of
+// the groups of 8 (keeping i % 8, hence the XCD of a head when bh_count is a
+// multiple of 8).  The sums over a unit's workgroups are then nearly equal
+// (GPT-2-shaped causal: at most 30 key tiles per unit against a mean of 27,
+// where one tile per head for every round put 48 on some units and 6 on
+// others).  Larger causal grids are dispatched as units free up: their tiles go
+// heaviest first within each XCD's contiguous range.
+__device__ __forceinline__ void grid_tile(int bid, int total, int ntiles, int bh_count, bool causal, int ncu, int& bh,
+                                          int& qt) {
+  if (causal && total <= 4 * ncu && (ncu & 7) == 0) {
+    int k = bid;
+    const int r = bid / ncu;
+    if ((r & 1) && (r + 1) * ncu <= total) {
+      const int c = bid - r * ncu;
+      k = r * ncu + ((((ncu >> 3) - 1 - (c >> 3)) << 3) | (c & 7));
+    }
+    const int qr = k / bh_count;
+    bh = k - qr * bh_count;
+    qt = ntiles - 1 - qr;
+    return;
+  }
+  const int per = total >> 3;
+  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
+  bh = lid / ntiles;
+  qt = lid - bh * ntiles;
+  if (causal) qt = ntiles - 1 - qt;  // heaviest tiles first
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
 // writes lds_base + 16 i (global_load_lds_dwordx4).  The builtin exists only for
 // the device target; clang's host pass drops a kernel whose body names it, so

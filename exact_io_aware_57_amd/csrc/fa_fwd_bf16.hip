@@ -94,18 +94,11 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
   const int r32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- workgroup -> (batch*head, query tile) --------------------------------
-  // The dispatcher hands workgroup i to XCD i % 8.  Renumber so that XCD x gets
-  // the contiguous logical range [x*per, (x+1)*per): neighbouring query tiles of
-  // one head then share that XCD's L2 for their K/V reads.
+  // ---- workgroup -> (batch*head, query tile): XCD-contiguous ranges, causal
+  // work balanced over the compute units (grid_tile) ----------------------------
   const int ntiles = (N + BM - 1) / BM;
-  const int total = gridDim.x;
-  const int bid = blockIdx.x;
-  const int per = total >> 3;
-  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
-  const int bh = lid / ntiles;
-  int qt = lid - bh * ntiles;
-  if (CAUSAL) qt = ntiles - 1 - qt;  // heaviest tiles first
+  int bh, qt;
+  grid_tile(blockIdx.x, gridDim.x, ntiles, p.B * p.H, CAUSAL, p.num_cu, bh, qt);
   const int b = bh / p.H;
 
   const size_t hoff = (size_t)bh * (size_t)N * D;

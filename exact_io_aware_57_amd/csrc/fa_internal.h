@@ -21,6 +21,7 @@ struct FwdParams {
   int causal;
   // FP8 inputs only: the tensors are descale * value(code)
   float descale_q = 1.0f, descale_k = 1.0f, descale_v = 1.0f;
+  int num_cu = 256;         // compute units of the device the launch runs on
 };
 
 // One decode problem (few queries against a key/value cache), already

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
         // redone against it, only when the sum is larger, not a number, or the
         // row has no reference yet.
         auto exps = [&](float mref, float& te) __attribute__((always_inline)) {
-          float ts = 0.0f, te0 = 0.0f, te1 = 0.0f;
+          float ts = 0.0f, te0 = 0.0f;
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -258,15 +258,18 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
               const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][2 * j + 1], sc, -mref));
               const uint32_t pp = pack_bf16(p0, p1);
               ts = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), ones, ts, false);
-              te0 += p0;
-              te1 += p1;
+              te0 += p0 + p1;
               pk[qb][kb][j] = pp;
             }
-          te = te0 + te1;
+          te = te0;
           return ts;
         };
         float le;
         float ls = exps(m_run[qb] == -INFINITY ? 0.0f : m_run[qb], le);
+        // The redo below overwrites le; without this use the compiler sinks the
+        // float32 sum past the branch and keeps every unrounded P live across
+        // it (about 30 more registers: three instead of four waves per SIMD).
+        pin(le);
         const bool bad = !(ls <= kMaxTileSum) || m_run[qb] == -INFINITY;
         if (__builtin_amdgcn_ballot_w64(bad) != 0) {
           keep_branch();
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
           pk[qb][kb][j] = pp;
         }
       le_run[qb] += te0 + te1;
+      pin(le_run[qb]);   // keeps the float32 sum ahead of the second product
     }
 
     // O^T = alpha O^T + V^T P^T.  MFMA (kb, u) takes accumulator registers

@@ -663,6 +663,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2, help="whole heads the CPU oracle times")
     ap.add_argument("--no-others", action="store_true", help="skip timing the other bf16 workloads")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the statistics after the timed region (launch statistics, clock, cold cache, "
+                         "device reference); for profiled runs")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (a known-size kernel for counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
@@ -711,9 +714,12 @@ def main(argv=None):
     value = main_p.flops / (ms_step * 1e-3) / 1e12
     achieved = main_p.flops / (ms_kernel * 1e-3) / 1e12
     # after the timed region: longer statistics, the clock, and the cold-cache variant
-    stats = kernel_stats(launch)
-    clock_mhz, clock_samples = sample_gfx_clock(launch, ms_kernel)
-    cold = cold_kernel_stats(launch, dev)
+    stats = cold = None
+    clock_mhz, clock_samples = None, 0
+    if not args.no_extras:
+        stats = kernel_stats(launch)
+        clock_mhz, clock_samples = sample_gfx_clock(launch, ms_kernel)
+        cold = cold_kernel_stats(launch, dev)
 
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -759,12 +765,12 @@ def main(argv=None):
                 "kernel_ms_avg": round(ms_kernel, 5), "kernel_ms_min": round(ms_kernel_min, 5),
                 "flop_per_launch": main_p.flops, "compulsory_bytes": main_p.bytes}
     tf = lambda ms: main_p.flops / (ms * 1e-3) / 1e12  # noqa: E731
-    roofline["kernel_stats"] = {"launches": stats["launches"], "ms_mean": round(stats["mean"], 5),
-                                "ms_median": round(stats["median"], 5), "ms_min": round(stats["min"], 5),
-                                "frac_median": round(tf(stats["median"]) / PEAK_BF16_TFLOPS, 4)}
-    roofline["cold_cache"] = {"launches": cold["launches"], "flush_mib": cold["flush_mib"],
-                              "ms_median": round(cold["median"], 5), "ms_min": round(cold["min"], 5),
-                              "frac_median": round(tf(cold["median"]) / PEAK_BF16_TFLOPS, 4)}
+    roofline["kernel_stats"] = None if stats is None else {
+        "launches": stats["launches"], "ms_mean": round(stats["mean"], 5), "ms_median": round(stats["median"], 5),
+        "ms_min": round(stats["min"], 5), "frac_median": round(tf(stats["median"]) / PEAK_BF16_TFLOPS, 4)}
+    roofline["cold_cache"] = None if cold is None else {
+        "launches": cold["launches"], "flush_mib": cold["flush_mib"], "ms_median": round(cold["median"], 5),
+        "ms_min": round(cold["min"], 5), "frac_median": round(tf(cold["median"]) / PEAK_BF16_TFLOPS, 4)}
     if clock_mhz is not None:
         peak_clk = 256 * 4096 * clock_mhz * 1e6 / 1e12
         roofline["clock"] = {"gfx_mhz_median": round(clock_mhz, 1), "samples": clock_samples,
@@ -773,8 +779,10 @@ def main(argv=None):
     else:
         roofline["clock"] = None
 
-    ref = device_reference(dev)
-    ref["attention_over_gemm"] = round(achieved / ref["bf16_gemm_tflops"], 4)
+    ref = None
+    if not args.no_extras:
+        ref = device_reference(dev)
+        ref["attention_over_gemm"] = round(achieved / ref["bf16_gemm_tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -43,16 +43,21 @@ def library_path():
 
 
 def load():
-    """Load libfa_mi355x.so (once).  Raises RuntimeError if it has not been built."""
+    """Load libfa_mi355x.so (once).  Raises RuntimeError if it has not been built.
+
+    The environment variable FA_MI355X_LIB names another build of the same
+    library to load instead (the kernel-candidate copies that the kernel-choice
+    measurements use); it must exist as well."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("FA_MI355X_LIB") or LIB_PATH
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"HIP library {LIB_PATH} is missing: build it with `python -m exact_io_aware_57_amd.build` "
+                f"HIP library {path} is missing: build it with `python -m exact_io_aware_57_amd.build` "
                 "(or __graft_entry__.build()); there is no CPU fallback")
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         for name in ("fa_fwd", "fa_fwd_f32"):
             fn = getattr(lib, name)

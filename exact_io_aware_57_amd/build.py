@@ -1,6 +1,7 @@
 """Build the HIP library libfa_mi355x.so in-tree with hipcc for gfx950.
 
     python -m exact_io_aware_57_amd.build [-v]
+    python -m exact_io_aware_57_amd.build --candidate ID   (a kernel-candidate copy, see build_candidate)
 
 Every source in csrc/ is compiled to an object under _build/ (in parallel), then
 the objects are linked into exact_io_aware_57_amd/libfa_mi355x.so.  Packed fp32
@@ -66,6 +67,32 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
+CANDIDATE_DIR = os.path.join(BUILD_DIR, "candidates")
+
+
+def candidate_path(cid):
+    return os.path.join(CANDIDATE_DIR, f"libfa_candidate{int(cid)}.so")
+
+
+def build_candidate(cid, verbose=False):
+    """A copy of the library whose bf16 forward pass always runs kernel form
+    ``cid`` (fa_fwd_bf16.hip built with -DFA_FORCE_FWD=cid; the other objects are
+    the library's own), for measuring each kernel candidate on one workload.
+    Requires build_library() first; returns the path."""
+    os.makedirs(CANDIDATE_DIR, exist_ok=True)
+    cc = hipcc()
+    src = os.path.join(CSRC, "fa_fwd_bf16.hip")
+    obj = os.path.join(CANDIDATE_DIR, f"fa_fwd_bf16_c{int(cid)}.o")
+    _run([cc, *device_flags(src), f"-DFA_FORCE_FWD={int(cid)}", "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj], verbose)
+    others = [os.path.join(BUILD_DIR, os.path.basename(x)[:-4] + ".o") for x in sources()
+              if os.path.basename(x) != "fa_fwd_bf16.hip"]
+    out = candidate_path(cid)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *others, "-o", out + ".tmp"], verbose)
+    os.replace(out + ".tmp", out)
+    os.remove(obj)
+    return out
+
+
 def build_library(verbose=False, jobs=None):
     """Compile every csrc/*.hip and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -84,4 +111,8 @@ def build_library(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv[1:]))
+    args = sys.argv[1:]
+    if "--candidate" in args:
+        print(build_candidate(int(args[args.index("--candidate") + 1]), verbose="-v" in args))
+    else:
+        print(build_library(verbose="-v" in args))

@@ -949,9 +949,40 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
                          dim3(kThreads * KS), args, 0, stream);
 }
 
+#if defined(FA_FORCE_FWD)
+// Candidate builds for the kernel-choice measurements (built only with
+// -DFA_FORCE_FWD=<id>, never in the library itself): every bf16 forward call
+// runs the one kernel form <id> names, so that rocprofv3 counters of each
+// candidate can be taken on the same workload.
+//   1 8-wave, 64-key tiles     2 8-wave, 128-key tiles (d 64)   3 8-wave, 32-key tiles (d 128)
+//   4 4-wave, 32-key tiles     5 4-wave, 64-key tiles           6 4-wave, 128-key tiles (d 64)
+//   7 4-wave two key groups, 64-key tiles   8 4-wave two key groups, 128-key tiles (d 64)
+template <int D, bool C>
+hipError_t launch_candidate(int id, const FwdParams& p, hipStream_t stream) {
+  switch (id) {
+    case 1: return launch_pp<D, 64, C>(p, stream);
+    case 2: if constexpr (D == 64) return launch_pp<64, 128, C>(p, stream); break;
+    case 3: if constexpr (D == 128) return launch_pp<128, 32, C>(p, stream); break;
+    case 4: return launch<D, 1, 32, 2, C>(p, stream);
+    case 5: return launch<D, 1, 64, 2, C>(p, stream);
+    case 6: if constexpr (D == 64) return launch<64, 1, 128, 2, C>(p, stream); break;
+    case 7: return launch<D, 1, 64, (D == 64 ? 2 : 1), C, 2>(p, stream);
+    case 8: if constexpr (D == 64) return launch<64, 1, 128, 1, C, 2>(p, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+#endif
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
+#if defined(FA_FORCE_FWD)
+  if (p.d == 64) return p.causal ? launch_candidate<64, true>(FA_FORCE_FWD, p, stream)
+                                 : launch_candidate<64, false>(FA_FORCE_FWD, p, stream);
+  if (p.d == 128) return p.causal ? launch_candidate<128, true>(FA_FORCE_FWD, p, stream)
+                                  : launch_candidate<128, false>(FA_FORCE_FWD, p, stream);
+#endif
   // Kernel choice by head size, key range and grid size (workgroups of the
   // ping-pong kernel: 256 query rows each), from same-process timings of every
   // candidate on gfx950 over grids of 32 to 2048 such workgroups.

@@ -19,8 +19,9 @@ roofline     the kernel's algorithmic FLOP per launch / its average duration,
              timed region: ``kernel_stats`` (mean, median and min over at least
              100 launches and 200 ms), ``cold_cache`` (a 512 MiB buffer, more
              than the 256 MB last-level cache, overwritten before each launch)
-             and ``clock`` (the graphics clock amdsmi reports while the kernel
-             runs back to back, with the matrix peak at that clock).
+             and ``clock`` (the average core clock while the kernel runs back
+             to back, from the device's core clock counter against its
+             constant 100 MHz counter, with the matrix peak at that clock).
              ``traffic`` is the HBM bytes per launch from a committed rocprofv3
              counter summary (FETCH_SIZE and WRITE_SIZE, scaled by the same
              counters on a copy of known size); null when missing or when the
@@ -192,6 +193,31 @@ def time_launches(launch, steps, warmup):
     return (t1 - t0) * 1e3 / steps, sum(per_launch) / len(per_launch), min(per_launch)
 
 
+def time_batched(launch, steps, warmup, reps=3):
+    """(host wall ms per launch, median and min kernel ms per launch) with events
+    around a batch of ``steps`` back-to-back launches, repeated ``reps`` times.
+    For short kernels an event pair around every launch adds several
+    microseconds; a batch keeps only the launches' own gaps."""
+    import torch
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    per, walls = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e3 / steps)
+        per.append(e0.elapsed_time(e1) / steps)
+    per.sort()
+    return sorted(walls)[len(walls) // 2], per[len(per) // 2], per[0]
+
+
 def kernel_stats(launch, min_launches=100, min_ms=200.0, max_launches=20000):
     """Per-launch kernel durations (HIP events on the launch stream around each
     launch), repeated until at least ``min_launches`` launches and ``min_ms`` of
@@ -236,70 +262,33 @@ def cold_kernel_stats(launch, dev, launches=20, flush_mib=512):
             "flush_mib": flush_mib}
 
 
-def sample_gfx_clock(launch, kernel_ms, seconds=0.6, period_s=0.004):
-    """Graphics clock while the kernel runs back to back: amdsmi's gpu_metrics
-    (current_gfxclks, MHz per XCD, averaged over the XCDs) sampled from a host
-    thread every few ms over about ``seconds`` of launches; the first 20% of the
-    samples (clock ramp) are dropped.  Returns (median MHz, sample count) or
-    (None, 0) if the metrics are not readable."""
-    import threading
-
+def sample_core_clock(launch, kernel_ms, stream_handle, dev, seconds=0.4):
+    """Average core clock (MHz) while the kernel runs back to back, measured on
+    the device: fa_clock_sample reads each compute unit's core clock counter and
+    the constant 100 MHz counter before and after a batch of launches on the
+    same stream; a unit's clock is 100 MHz * cycles / ticks.  Returns (median
+    over the units, 10th and 90th percentile, units paired, launches)."""
     import torch
 
-    try:
-        import amdsmi
+    from exact_io_aware_57_amd import binding
 
-        amdsmi.amdsmi_init()
-        handles = amdsmi.amdsmi_get_processor_handles()
-        if not handles:
-            return None, 0
-        handle = handles[0]
-    except Exception:
-        return None, 0
-
-    def read():
-        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-        vals = m.get("current_gfxclks")
-        if isinstance(vals, (list, tuple)):
-            vals = [float(v) for v in vals if isinstance(v, (int, float)) and 0 < v < 10000]
-            if vals:
-                return sum(vals) / len(vals)
-        v = m.get("current_gfxclk")
-        return float(v) if isinstance(v, (int, float)) and 0 < v < 10000 else None
-
-    samples, stop = [], threading.Event()
-
-    def sampler():
-        while not stop.is_set():
-            try:
-                v = read()
-            except Exception:
-                v = None
-            if v is not None:
-                samples.append(v)
-            time.sleep(period_s)
-
-    n = max(20, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
-    th = threading.Thread(target=sampler, daemon=True)
-    done = torch.cuda.Event()
-    th.start()
-    try:
-        for _ in range(n):
-            launch()
-        done.record()
-        while not done.query():
-            time.sleep(0.002)
-    finally:
-        stop.set()
-        th.join()
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
-    keep = sorted(samples[len(samples) // 5:])
-    if not keep:
-        return None, 0
-    return keep[len(keep) // 2], len(keep)
+    n_vals = 3 * binding.FA_CLOCK_SAMPLE_UNITS
+    buf = torch.zeros(2 * n_vals, dtype=torch.int64, device=dev)
+    n = max(10, int(seconds * 1e3 / max(kernel_ms, 1e-3)))
+    for _ in range(3):
+        launch()
+    if binding.fa_clock_sample(buf.data_ptr(), stream_handle) != 0:
+        return None, None, None, 0, 0
+    for _ in range(n):
+        launch()
+    binding.fa_clock_sample(buf.data_ptr() + n_vals * 8, stream_handle)
+    torch.cuda.synchronize()
+    v = buf.cpu().tolist()
+    mhz = sorted(binding.clock_mhz_by_unit(v[:n_vals], v[n_vals:]).values())
+    if not mhz:
+        return None, None, None, 0, 0
+    pick = lambda f: mhz[min(len(mhz) - 1, int(f * len(mhz)))]  # noqa: E731
+    return pick(0.5), pick(0.1), pick(0.9), len(mhz), n
 
 
 def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=True, std=0.5, seed=6, steps=20,
@@ -322,7 +311,7 @@ def time_grouped(dev, stream_handle, B=1, H=32, H_kv=8, N=16384, d=128, causal=T
         if st != 0:
             raise RuntimeError(f"fa_fwd_gqa failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, _ = time_launches(launch, *other_counts(steps, 10))
+    m_step, m_kern, _ = time_batched(launch, *other_counts(steps, 10))
     flops = algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"{name}: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 {'causal' if causal else 'non-causal'}",
             "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
@@ -354,7 +343,7 @@ def time_decode(dev, stream_handle, B=8, H=32, H_kv=8, Nq=1, Nk=32768, d=128, ca
         if st != 0:
             raise RuntimeError(f"fa_decode failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 10))
+    m_step, m_kern, m_min = time_batched(launch, *other_counts(steps, 10))
     cbytes = 2 * B * H_kv * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
     splits = need // (B * H * Nq * (d + 1) * 4)
     return {"workload": f"decode: B={B} H={H} H_kv={H_kv} Nq={Nq} cache={Nk} d={d} bf16 "
@@ -392,7 +381,7 @@ def time_backward(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal
         if st != 0:
             raise RuntimeError(f"fa_bwd failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 5))
+    m_step, m_kern, m_min = time_batched(launch, *other_counts(steps, 5))
     flops = 2.5 * algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"long_context_bwd: B={B} H={H} H_kv={H_kv} N={N} d={d} bf16 "
                         f"{'causal' if causal else 'non-causal'} (dQ, dK, dV)",
@@ -421,7 +410,7 @@ def time_fp8(dev, stream_handle, B=1, H=32, H_kv=32, N=16384, d=128, causal=True
         if st != 0:
             raise RuntimeError(f"fa_fwd_fp8 failed: {binding.fa_status_str(st)}")
 
-    m_step, m_kern, m_min = time_launches(launch, *other_counts(steps, 10))
+    m_step, m_kern, m_min = time_batched(launch, *other_counts(steps, 10))
     flops = algorithmic_flops(B, H, N, d, causal)
     return {"workload": f"long_context_fp8: B={B} H={H} H_kv={H_kv} N={N} d={d} e4m3 in, bf16 out "
                         f"{'causal' if causal else 'non-causal'}",
@@ -715,10 +704,11 @@ def main(argv=None):
     achieved = main_p.flops / (ms_kernel * 1e-3) / 1e12
     # after the timed region: longer statistics, the clock, and the cold-cache variant
     stats = cold = None
-    clock_mhz, clock_samples = None, 0
+    clock_mhz, clock_lo, clock_hi, clock_units, clock_launches = None, None, None, 0, 0
     if not args.no_extras:
         stats = kernel_stats(launch)
-        clock_mhz, clock_samples = sample_gfx_clock(launch, ms_kernel)
+        clock_mhz, clock_lo, clock_hi, clock_units, clock_launches = sample_core_clock(launch, ms_kernel,
+                                                                                      stream.cuda_stream, dev)
         cold = cold_kernel_stats(launch, dev)
 
     if args.calib_copy_mb:
@@ -736,7 +726,7 @@ def main(argv=None):
                 continue
             p = Problem(idx, dev)
             steps = 50 if w.N >= 4096 else 200
-            m_step, m_kern, m_min = time_launches(p.launcher(stream.cuda_stream), *other_counts(steps, 10))
+            m_step, m_kern, m_min = time_batched(p.launcher(stream.cuda_stream), *other_counts(steps, 10))
             entry = {"workload": w.describe(), "ms_per_step": round(m_step, 5), "kernel_ms": round(m_kern, 5),
                      "tflops": round(p.flops / (m_kern * 1e-3) / 1e12, 2),
                      "hbm_gbs_compulsory": round(p.bytes / (m_kern * 1e-3) / 1e9, 1)}
@@ -773,8 +763,10 @@ def main(argv=None):
         "ms_min": round(cold["min"], 5), "frac_median": round(tf(cold["median"]) / PEAK_BF16_TFLOPS, 4)}
     if clock_mhz is not None:
         peak_clk = 256 * 4096 * clock_mhz * 1e6 / 1e12
-        roofline["clock"] = {"gfx_mhz_median": round(clock_mhz, 1), "samples": clock_samples,
-                             "source": "amdsmi gpu_metrics current_gfxclks during back-to-back launches",
+        roofline["clock"] = {"core_mhz": round(clock_mhz, 1), "core_mhz_p10": round(clock_lo, 1),
+                             "core_mhz_p90": round(clock_hi, 1), "units": clock_units, "launches": clock_launches,
+                             "source": "each compute unit's core clock counter against the 100 MHz counter over "
+                                       "back-to-back launches (fa_clock_sample); median over the units",
                              "peak_at_clock": round(peak_clk, 1), "frac_at_clock": round(achieved / peak_clk, 4)}
     else:
         roofline["clock"] = None

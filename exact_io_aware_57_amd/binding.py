@@ -25,8 +25,9 @@ FA_ERR_LAUNCH = -5
 FA_ERR_SCRATCH_TOO_SMALL = -6
 FA_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
-EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_noalloc", "fa_decode_workspace_size",
-                    "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str")
+EXPORTED_SYMBOLS = ("fa_bwd", "fa_bwd_workspace_size", "fa_clock_sample", "fa_decode", "fa_decode_noalloc",
+                    "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32",
+                    "fa_status_str")
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +81,8 @@ def load():
         lib.fa_decode_noalloc.restype = i32
         lib.fa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+        lib.fa_clock_sample.argtypes = [vp, vp]
+        lib.fa_clock_sample.restype = i32
         lib.fa_status_str.argtypes = [i32]
         lib.fa_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -297,6 +300,38 @@ def decode_forward(q, k, v, scale, causal=False, seqlens=None, num_splits=0, out
     if st != FA_OK:
         raise FaError(st, "fa_decode")
     return out, lse
+
+
+FA_CLOCK_SAMPLE_UNITS = 256
+
+
+def fa_clock_sample(out, stream):
+    """C fa_clock_sample: out is the device address of 3 * FA_CLOCK_SAMPLE_UNITS uint64 values."""
+    return load().fa_clock_sample(_ptr(out), _ptr(stream))
+
+
+def clock_mhz_by_unit(first, second):
+    """Average core clock (MHz) of each compute unit between two fa_clock_sample
+    results (3 * FA_CLOCK_SAMPLE_UNITS integers each), paired by the unit's
+    place; units that held more than one sampling workgroup are left out:
+    {place: MHz}."""
+    def by_unit(v):
+        seen, out = set(), {}
+        for w in range(len(v) // 3):
+            key = int(v[3 * w + 2])
+            if key in seen:
+                out.pop(key, None)
+                continue
+            seen.add(key)
+            out[key] = (int(v[3 * w]), int(v[3 * w + 1]))
+        return out
+    a, b = by_unit(first), by_unit(second)
+    res = {}
+    for key in sorted(set(a) & set(b)):
+        cyc, ticks = b[key][0] - a[key][0], b[key][1] - a[key][1]
+        if cyc > 0 and ticks > 0:
+            res[key] = 100.0 * cyc / ticks
+    return res
 
 
 def fa_status_str(status):

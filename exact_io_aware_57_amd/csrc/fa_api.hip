@@ -22,6 +22,24 @@
 static __device__ __align__(256) char scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
+// Workgroup w reads the core clock counter of the compute unit it runs on
+// (s_memtime, counting core clock cycles; the counters of different units are
+// not aligned with one another), the constant 100 MHz counter (s_memrealtime)
+// and the unit's place: XCD id << 16 | shader engine << 8 | unit, from the
+// XCC_ID and HW_ID registers.  Two samples around other work, paired by unit,
+// give each unit's average core clock in between.
+__global__ void clock_sample_kernel(unsigned long long* out) {
+  if (threadIdx.x == 0) {
+    const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);        // HW_ID
+    const unsigned xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;  // XCC_ID
+    out[3 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+    out[3 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    out[3 * blockIdx.x + 2] = (xcc << 16) | (((hw >> 13) & 7) << 8) | ((hw >> 8) & 15);
+  }
+}
+}  // namespace
+
+namespace {
 
 constexpr int kMaxDevices = 64;
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other;
@@ -243,6 +261,19 @@ int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, floa
                       int B, int H, int H_kv, int Nq, int Nk, int d, float scale, int causal,
                       const int32_t* seqlens, int num_splits, void* stream) {
   return decode_impl(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal, seqlens, num_splits, nullptr, 0, stream);
+}
+
+int fa_clock_sample(unsigned long long* out, void* stream) {
+  if (!out) return FA_ERR_INVALID_ARG;
+  if (!aligned(out, 8)) return FA_ERR_MISALIGNED;
+  const int st = check_device();
+  if (st != FA_OK) return st;
+  void* args[] = {&out};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&clock_sample_kernel), dim3(FA_CLOCK_SAMPLE_UNITS), dim3(64),
+                         args, 0,
+                         reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? FA_OK
+             : FA_ERR_LAUNCH;
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

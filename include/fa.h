@@ -221,6 +221,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /* Bytes of workspace fa_bwd needs (0 for invalid arguments). */
 size_t fa_bwd_workspace_size(int B, int H, int N);
 
+/*
+ * Measurement aid, not part of the attention path: enqueues on `stream` a
+ * kernel of FA_CLOCK_SAMPLE_UNITS workgroups in which workgroup w writes
+ * out[3w] = the core clock counter of the compute unit it runs on (s_memtime,
+ * core clock cycles; the counters of different units are not aligned),
+ * out[3w+1] = the constant 100 MHz counter (s_memrealtime) and out[3w+2] =
+ * the unit's place (XCD id << 16 | shader engine << 8 | unit).  out is a
+ * device pointer to 3 * FA_CLOCK_SAMPLE_UNITS uint64 values.  Two samples
+ * around a batch of attention launches on the same stream, paired by unit,
+ * give each unit's average core clock over the batch:
+ * 100 MHz * d(cycles) / d(ticks).  Returns FA_OK or a negative fa_status.
+ */
+#define FA_CLOCK_SAMPLE_UNITS 256
+int fa_clock_sample(unsigned long long* out, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_str(int status);
 

@@ -30,9 +30,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_noalloc",
-                                    "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_gqa",
-                                    "fa_fwd_gqa_f32", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_clock_sample", "fa_decode",
+                                    "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_f32",
+                                    "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_status_str"]
     assert tuple(declared_functions()) == tuple(sorted(binding.EXPORTED_SYMBOLS))
 
 
@@ -259,3 +259,8 @@ def test_decode_noalloc_scratch_limit(lib):
         E.FA_ERR_UNSUPPORTED
     assert E.fa_decode_noalloc(FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 64, 0.125, 0, None, 0, None) == \
         E.FA_ERR_MISALIGNED
+
+
+def test_clock_sample_rejects_bad_pointers(lib):
+    assert binding.fa_clock_sample(None, None) == binding.FA_ERR_INVALID_ARG
+    assert binding.fa_clock_sample(FAKE + 4, None) == binding.FA_ERR_MISALIGNED

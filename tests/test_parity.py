@@ -554,3 +554,30 @@ def test_wrappers_refuse_host_outputs_and_wide_lengths():
         binding.attention_forward(qd, kd, vd, 0.125, seqlens=torch.tensor([64, 50], dtype=torch.int32))
     with pytest.raises(ValueError, match="workspace"):
         binding.decode_forward(qd[:, :, :1].contiguous(), kd, vd, 0.125, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+
+
+def test_clock_sample_reads_each_unit():
+    """fa_clock_sample: the counters advance between two samples around
+    back-to-back kernel launches, most compute units (of all 8 XCDs) pair up
+    between the two samples, and cycles per 100 MHz tick give a core clock
+    within the chip's range."""
+    n_vals = 3 * binding.FA_CLOCK_SAMPLE_UNITS
+    buf = torch.zeros(2 * n_vals, dtype=torch.int64, device=DEV)
+    inp = make_inputs(4)
+    q, k, v = (x.to(DEV) for x in (inp["q"], inp["k"], inp["v"]))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *q.shape, inp["scale"], False, None, st)
+    assert binding.fa_clock_sample(buf.data_ptr(), st) == binding.FA_OK
+    for _ in range(20):
+        assert binding.fa_fwd(*args) == binding.FA_OK
+    assert binding.fa_clock_sample(buf.data_ptr() + n_vals * 8, st) == binding.FA_OK
+    torch.cuda.synchronize()
+    vals = buf.cpu().tolist()
+    mhz = binding.clock_mhz_by_unit(vals[:n_vals], vals[n_vals:])
+    xcds = sorted({key >> 16 for key in mhz})
+    m = sorted(mhz.values())
+    say(f"[clock] {len(m)} units paired on XCDs {xcds}: median {m[len(m) // 2]:.0f} MHz, "
+        f"range {m[0]:.0f}..{m[-1]:.0f}")
+    assert xcds == list(range(8)) and len(m) >= 128
+    assert 100.0 <= m[len(m) // 2] <= 2600.0

@@ -141,6 +141,47 @@ __device__ __forceinline__ void grid_tile(int bid, int total, int ntiles, int bh
   if (causal) qt = ntiles - 1 - qt;  // heaviest tiles first
 }
 
+// The same for a grid without the causal mask whose batches have their own key
+// lengths (seqlens, B entries): a tile of batch b costs about ceil(L_b / bn)
+// key tiles.  When the whole grid is resident at once (as above) the tiles are
+// ranked by that cost, longest batches first (ties by batch index), and the
+// ranks go to the units in the same alternating order as the causal tiles, so
+// that every unit gets a similar sum.  Within a batch consecutive ranks take
+// consecutive heads, so the query tiles of one head stay on one XCD when H is a
+// multiple of 8.  Every wave computes the same mapping: lane j < B holds batch
+// j's cost and its rank among the batches.  Returns false (mapping not taken)
+// for grids of more than four rounds or more than 64 batches.
+__device__ __forceinline__ bool grid_tile_lengths(int bid, int total, int ntiles, int B, int H, int N, int bn,
+                                                  const int32_t* seqlens, int ncu, int& bh, int& qt) {
+  if (!(total <= 4 * ncu && (ncu & 7) == 0 && B <= 64)) return false;
+  const int lane = (int)(threadIdx.x & 63);
+  int c = -1;
+  if (lane < B) {
+    const int L = seqlens[lane];
+    c = ((L < 0 ? 0 : (L > N ? N : L)) + bn - 1) / bn;
+  }
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {
+    const int cj = __builtin_amdgcn_readlane(c, j);
+    rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
+  }
+  int k = bid;
+  const int r = bid / ncu;
+  if ((r & 1) && (r + 1) * ncu <= total) {
+    const int cc = bid - r * ncu;
+    k = r * ncu + ((((ncu >> 3) - 1 - (cc >> 3)) << 3) | (cc & 7));
+  }
+  const int per_b = H * ntiles;
+  const int pos = k / per_b;   // < B: the grid has B * H * ntiles workgroups
+  const int rest = k - pos * per_b;
+  // the ranks of lanes 0..B-1 are a permutation of 0..B-1: exactly one bit
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(lane < B && rank == pos);
+  const int b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(m));
+  qt = rest / H;
+  bh = b * H + (rest - qt * H);
+  return true;
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
 // writes lds_base + 16 i (global_load_lds_dwordx4).  The builtin exists only for
 // the device target; clang's host pass drops a kernel whose body names it, so

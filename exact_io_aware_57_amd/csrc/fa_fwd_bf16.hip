@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
   // work balanced over the compute units (grid_tile) ----------------------------
   const int ntiles = (N + BM - 1) / BM;
   int bh, qt;
-  grid_tile(blockIdx.x, gridDim.x, ntiles, p.B * p.H, CAUSAL, p.num_cu, bh, qt);
+  if (CAUSAL || !p.seqlens || !grid_tile_lengths(blockIdx.x, gridDim.x, ntiles, p.B, p.H, N, BN, p.seqlens, p.num_cu, bh, qt))
+    grid_tile(blockIdx.x, gridDim.x, ntiles, p.B * p.H, CAUSAL, p.num_cu, bh, qt);
   const int b = bh / p.H;
 
   const size_t hoff = (size_t)bh * (size_t)N * D;

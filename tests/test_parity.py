@@ -433,6 +433,22 @@ def test_padding_lengths_bf16(d, causal):
     check_against_oracle(q, k, v, 0.125, causal, seqlens, fp32=False, tag=f"padding d={d}")
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_many_batch_lengths_bf16(B):
+    """Per-batch key lengths on a grid that is resident at once: with at most 64
+    batches the workgroups are assigned by batch length (longest first), over 64
+    the plain order is used.  Repeated lengths (ties), empty and full batches,
+    every row of every head."""
+    H, N = 4, 512
+    q, k, v, _ = random_qkv(B, H, N, 64, torch.bfloat16, 1.0, seed=70 + B)
+    g = torch.Generator().manual_seed(B)
+    lens = torch.randint(0, N + 1, (B,), generator=g, dtype=torch.int32)
+    lens[0], lens[1], lens[2], lens[3] = 0, N, N, 257
+    lens[B - 1] = lens[B - 2]
+    for causal in (False, True):
+        check_against_oracle(q, k, v, 0.125, causal, lens, fp32=False, tag=f"many batch lengths B={B} causal={causal}")
+
+
 def test_padding_lengths_out_of_range_are_clamped():
     n = 130
     q, k, v, _ = random_qkv(3, 1, n, 64, torch.bfloat16, 1.0, seed=8)

@@ -27,7 +27,9 @@ roofline     the kernel's algorithmic FLOP per launch / its average duration,
              counters on a copy of known size); null when missing or when the
              kernel source has changed since the counters were taken.
 cpu_baseline the CPU oracle (float64 numpy, full score matrix) timed on this
-             host on a bounded sample (whole heads of the same workload).
+             host on a bounded sample (whole heads of the same workload), and
+             ``gpu_over_oracle``, the GPU's rate over the oracle's (a reported
+             baseline, not a measure of kernel quality).
 device_reference
              context from the same device after the timed region: the bf16 rate
              of a plain library GEMM (torch.matmul) and the read bandwidth of a
@@ -779,6 +781,8 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.workload, args.cpu_heads)
+        # the same unit on both sides (TFLOP/s of algorithmic work)
+        cpu["gpu_over_oracle"] = round(value / cpu["value"], 1) if cpu["value"] else None
 
     line = {
         "metric": METRIC,

@@ -204,5 +204,21 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(src) : "memory", "m0");
 }
 
+// The same load addressed as a wave-uniform base (SGPR pair) plus a 32-bit
+// per-lane byte offset (VGPR): global_load_lds_dwordx4 voffset, sbase.  On
+// gfx950 a vector-memory instruction that reads a 64-bit address from VGPRs is
+// slow to issue while another wave on the SIMD runs products whose
+// accumulators are VGPRs (four such loads: about 1090 ticks, against 85 with
+// no products beside them); this form reads one VGPR and issues in about 120.
+// `base` must be the same in every lane; `off` < 2^32.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, void* lds_base) {
+  const unsigned l = (unsigned)(uintptr_t)((lds_void*)lds_base);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(off), "s"(bu)
+               : "memory", "m0");
+}
+
 }  // namespace
 }  // namespace fa

@@ -477,7 +477,11 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
 // not do within one wave.
 // K and V have two LDS buffers each.  At every even phase 2t the workgroup
 // issues the loads of K_{t+1} and V_t (direct global->LDS), and waits for them
-// at the end of phase 2t+1, before any wave reads them.
+// at the end of phase 2t+1, before any wave reads them.  The loads take the
+// scalar-base form (head base in SGPRs, 32-bit lane offset): the group that is
+// entering its softmax phase issues its loads while the other group's products
+// have started, where the 64-bit-address form is slow to issue (long context
+// 1.826 -> 1.809 ms, head size 256 1.884 -> 1.859 ms, results bitwise equal).
 // Head size 256 runs this kernel with 32-key tiles: Q fragments (64 registers),
 // O^T (128), the score tile (16) and P (8) then fit the 256 registers of a wave
 // at two waves per SIMD, provided the matrix phase reads each LDS operand two
@@ -591,7 +595,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       int row, kc, vc;
       ld_addr(i, row, kc, vc);
       const int key = min(t * BN + row, N - 1);
-      dma16(Kh + (size_t)key * D + kc, kbuf[t & 1] + (wave * NLD + i) * 1024);
+      dma16s(Kh, (uint32_t)(((size_t)key * D + kc) * 2), kbuf[t & 1] + (wave * NLD + i) * 1024);
     }
   };
   auto load_v = [&](int t) {
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       int row, kc, vc;
       ld_addr(i, row, kc, vc);
       const int key = min(t * BN + row, N - 1);
-      dma16(Vh + (size_t)key * D + vc, vbuf[t & 1] + (wave * NLD + i) * 1024);
+      dma16s(Vh, (uint32_t)(((size_t)key * D + vc) * 2), vbuf[t & 1] + (wave * NLD + i) * 1024);
     }
   };
 
@@ -988,13 +992,17 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   // ping-pong kernel: 256 query rows each), from same-process timings of every
   // candidate on gfx950 over grids of 32 to 2048 such workgroups.
   const long long pp_groups = (long long)p.B * p.H * ((p.N + 255) / 256);
+  // The ping-pong kernel addresses a head's K and V by 32-bit byte offsets
+  // from the head's base (the scalar-base form of its tile loads).
+  const bool pp_fits = (unsigned long long)p.N * (unsigned long long)p.d * 2ull <= 0xFFFFFFFFull;
   if (p.d == 256) {
     // 32-key tiles: the score tile, the Q fragments (64 registers) and O^T (128)
     // of a wave then fit two waves per SIMD.  On grids of 256 (non-causal) and
     // 512 (causal) workgroups the ping-pong kernel takes 11-29% less time than
     // the one-wave-per-SIMD head-size-256 kernel (128 query rows per
     // workgroup), which takes 12-18% less on grids of 64 and 128.
-    if (pp_groups >= 256) return p.causal ? launch_pp<256, 32, true>(p, stream) : launch_pp<256, 32, false>(p, stream);
+    if (pp_groups >= 256 && pp_fits)
+      return p.causal ? launch_pp<256, 32, true>(p, stream) : launch_pp<256, 32, false>(p, stream);
     return launch_fwd_bf16_d256(p, stream);
   }
   if (p.d == 64) {
@@ -1008,7 +1016,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
     // less time than 64-key tiles on grids under 1024 workgroups, within 3%
     // above) and 64-key tiles below, where a workgroup sees only a few tiles.
     const bool pp_long = p.causal ? (pp_groups >= 256 && p.N >= 4096) : (pp_groups >= 256 && p.N >= 2048);
-    if (pp_long) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
+    if (pp_long && pp_fits) return p.causal ? launch_pp<64, 128, true>(p, stream) : launch_pp<64, 128, false>(p, stream);
     // Below that the 4-wave kernel runs, also on full grids: under 2048 keys it
     // takes 4-8% less time than the ping-pong kernel with 64-key tiles
     // (non-causal) and 16-33% less (causal, 1024 and 1536 keys, 256 to 512
@@ -1042,7 +1050,8 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   // heads).
   if (pp_groups <= 128 && p.N >= 768)
     return p.causal ? launch<128, 1, 64, 1, true, 2>(p, stream) : launch<128, 1, 64, 1, false, 2>(p, stream);
-  if (p.N >= 1024) return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
+  if (p.N >= 1024 && pp_fits)
+    return p.causal ? launch_pp<128, 64, true>(p, stream) : launch_pp<128, 64, false>(p, stream);
   return p.causal ? launch<128, 1, 32, 2, true>(p, stream) : launch<128, 1, 32, 2, false>(p, stream);
 }
 

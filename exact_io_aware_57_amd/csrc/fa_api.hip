@@ -225,6 +225,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // the kernels address a head's rows by 32-bit byte offsets from its base
+  if ((uint64_t)N * (uint64_t)d * 2u > 0xFFFFFFFFull) return FA_ERR_UNSUPPORTED;
   if ((uint64_t)B * H * N * d > (uint64_t(1) << 40)) return FA_ERR_INVALID_ARG;
   const long long tiles = ((long long)N + 127) / 128;
   if ((long long)B * H * tiles > INT32_MAX || (long long)B * H * (N + 64) > INT32_MAX) return FA_ERR_INVALID_ARG;

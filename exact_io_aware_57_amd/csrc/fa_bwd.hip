@@ -168,7 +168,7 @@ __device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char
     const int row = pos / T::CH;
     const int cst = pos % T::CH;
     const int r = min(r0 + row, N - 1);
-    load_to_lds16(src + (size_t)r * D + ((cst ^ bswz<D>(row)) << 3), dst + (wave * T::NLD + i) * 1024);
+    dma16s(src, (uint32_t)(((size_t)r * D + ((cst ^ bswz<D>(row)) << 3)) * 2), dst + (wave * T::NLD + i) * 1024);
   }
 }
 
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     load_tile<D>(reinterpret_cast<const __bf16*>(p.dout) + hoff, q0 + kBT, N, base + QMAT + T::MAT, wave, lane);
     if (wave < 2 && lane < 32) {   // 128 floats of lse2 (wave 0) or D (wave 1)
       const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + hq) * (size_t)p.Npad + q0;
-      load_to_lds16(src + lane * 4, base + 2 * QMAT + wave * kQT * 4);
+      dma16s(src, (uint32_t)(lane * 16), base + 2 * QMAT + wave * kQT * 4);
     }
   };
 

@@ -202,7 +202,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  *   dq         : [B, H, N, d] bf16 output
  *   dk, dv     : [B, H_kv, N, d] bf16 outputs; with grouped heads, the sum over
  *                the query heads that share the key/value head
- *   d          : 64 or 128
+ *   d          : 64 or 128 (FA_ERR_UNSUPPORTED otherwise, and for heads of
+ *                4 GiB or more, N * d * 2 >= 2^32 bytes: the kernels address a
+ *                head's rows by 32-bit offsets)
  *   scale, causal, seqlens : as for the forward call that produced o and lse
  *   workspace, workspace_size : caller-owned device memory of at least
  *                fa_bwd_workspace_size(B, H, N) bytes (16-byte aligned) for the

@@ -204,6 +204,12 @@ def test_bwd_arguments_are_checked_on_the_host(lib):
         assert call_bwd(**over) == E.FA_ERR_INVALID_ARG, over
     for d in (32, 96, 256):
         assert call_bwd(d=d) == E.FA_ERR_UNSUPPORTED, d
+    # a head of 4 GiB or more (N * d * 2 bytes >= 2^32) is refused: the kernels
+    # address a head's rows by 32-bit offsets; one row less still passes on
+    big = dict(B=1, H=1, H_kv=1, workspace_size=1 << 40)
+    assert call_bwd(N=(1 << 24) + 1, d=128, **big) == E.FA_ERR_UNSUPPORTED
+    assert call_bwd(N=(1 << 25) + 1, d=64, **big) == E.FA_ERR_UNSUPPORTED
+    assert call_bwd(N=(1 << 24) - 1, d=128, **big) == E.FA_ERR_NO_DEVICE
     for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv", "workspace"):
         assert call_bwd(**{name: FAKE + 8}) == E.FA_ERR_MISALIGNED, name
     assert call_bwd(lse=FAKE + 2) == E.FA_ERR_MISALIGNED

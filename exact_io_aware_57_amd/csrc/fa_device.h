@@ -120,15 +120,22 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // where one tile per head for every round put 48 on some units and 6 on
 // others).  Larger causal grids are dispatched as units free up: their tiles go
 // heaviest first within each XCD's contiguous range.
+// Rank (heaviest first) of workgroup bid on a grid of at most four rounds of
+// ncu: even rounds take ranks in order, odd rounds in reverse order of the
+// groups of 8, keeping bid % 8.
+__device__ __forceinline__ int snake_rank(int bid, int total, int ncu) {
+  const int r = bid / ncu;
+  if ((r & 1) && (r + 1) * ncu <= total) {
+    const int c = bid - r * ncu;
+    return r * ncu + ((((ncu >> 3) - 1 - (c >> 3)) << 3) | (c & 7));
+  }
+  return bid;
+}
+
 __device__ __forceinline__ void grid_tile(int bid, int total, int ntiles, int bh_count, bool causal, int ncu, int& bh,
                                           int& qt) {
   if (causal && total <= 4 * ncu && (ncu & 7) == 0) {
-    int k = bid;
-    const int r = bid / ncu;
-    if ((r & 1) && (r + 1) * ncu <= total) {
-      const int c = bid - r * ncu;
-      k = r * ncu + ((((ncu >> 3) - 1 - (c >> 3)) << 3) | (c & 7));
-    }
+    const int k = snake_rank(bid, total, ncu);
     const int qr = k / bh_count;
     bh = k - qr * bh_count;
     qt = ntiles - 1 - qr;
@@ -165,12 +172,7 @@ __device__ __forceinline__ bool grid_tile_lengths(int bid, int total, int ntiles
     const int cj = __builtin_amdgcn_readlane(c, j);
     rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
   }
-  int k = bid;
-  const int r = bid / ncu;
-  if ((r & 1) && (r + 1) * ncu <= total) {
-    const int cc = bid - r * ncu;
-    k = r * ncu + ((((ncu >> 3) - 1 - (cc >> 3)) << 3) | (cc & 7));
-  }
+  const int k = snake_rank(bid, total, ncu);
   const int per_b = H * ntiles;
   const int pos = k / per_b;   // < B: the grid has B * H * ntiles workgroups
   const int rest = k - pos * per_b;

@@ -213,6 +213,16 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 // accumulators are VGPRs (four such loads: about 1090 ticks, against 85 with
 // no products beside them); this form reads one VGPR and issues in about 120.
 // `base` must be the same in every lane; `off` < 2^32.
+// A wave-uniform pointer moved to SGPRs once (readfirstlane of both halves),
+// so that loops taking it as a scalar base do not re-read it from VGPRs.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  return reinterpret_cast<P*>((uintptr_t)u);
+}
+
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, void* lds_base) {
   const unsigned l = (unsigned)(uintptr_t)((lds_void*)lds_base);
   const uint64_t b = (uint64_t)(uintptr_t)base;

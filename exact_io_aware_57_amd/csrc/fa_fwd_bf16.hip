@@ -523,8 +523,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   // key/value head of this query head: groups of H / Hkv consecutive heads
   const size_t kvoff = ((size_t)b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * (size_t)N * D;
   const __bf16* __restrict__ Qh = reinterpret_cast<const __bf16*>(p.q) + hoff;
-  const __bf16* __restrict__ Kh = reinterpret_cast<const __bf16*>(p.k) + kvoff;
-  const __bf16* __restrict__ Vh = reinterpret_cast<const __bf16*>(p.v) + kvoff;
+  const __bf16* __restrict__ Kh = uniform_ptr(reinterpret_cast<const __bf16*>(p.k) + kvoff);
+  const __bf16* __restrict__ Vh = uniform_ptr(reinterpret_cast<const __bf16*>(p.v) + kvoff);
   __bf16* __restrict__ Oh = reinterpret_cast<__bf16*>(p.o) + hoff;
 
   int kv_valid = N;

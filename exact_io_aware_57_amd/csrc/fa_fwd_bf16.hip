@@ -477,7 +477,8 @@ __global__ __launch_bounds__(kThreads * KS, OCC) void fwd_bf16_kernel(FwdParams 
 // not do within one wave.
 // K and V have two LDS buffers each.  At every even phase 2t the workgroup
 // issues the loads of K_{t+1} and V_t (direct global->LDS), and waits for them
-// at the end of phase 2t+1, before any wave reads them.  The loads take the
+// at the end of phase 2t+1, before any wave reads them.  At head size 128 and
+// 256 that odd-phase barrier is the only one per tile.  The loads take the
 // scalar-base form (head base in SGPRs, 32-bit lane offset): the group that is
 // entering its softmax phase issues its loads while the other group's products
 // have started, where the 64-bit-address form is slow to issue (long context
@@ -865,6 +866,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
 
   // Global phase counter, identical in every wave.  Phase 2t starts the loads of
   // K_{t+1} and V_t; phase 2t+1 ends by waiting for them.
+  // The barrier after an odd phase is what the data needs: the tile loads are
+  // complete and visible, and the buffers the next loads overwrite were last
+  // read in the two phases before it.  The barrier after an even phase only
+  // keeps the two groups one phase apart; the softmax phase reads no LDS, so
+  // without it a group that finishes its softmax early starts its products
+  // beside the other group's last products instead of waiting.  At head size
+  // 128 and 256 that measured faster (long context 1.790 -> 1.775 ms, d = 256
+  // 1.841 -> 1.804 ms, non-causal d = 128 0.873 -> 0.861 ms, median of
+  // same-process runs; results bitwise equal); at head size 64, where the
+  // softmax phase is the longer one, it was 2-4% slower, so it stays there.
+  constexpr bool kEvenBarrier = D < 128;
   const int n_phases = 2 * ntk + 2;
   int ph = 0;
   auto begin_phase = [&]() __attribute__((always_inline)) {
@@ -879,7 +891,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   auto end_phase = [&]() __attribute__((always_inline)) {
     if (ph & 1) wait_vmem();
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if (kEvenBarrier || (ph & 1)) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     ++ph;
   };

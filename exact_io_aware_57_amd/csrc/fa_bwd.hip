@@ -154,21 +154,29 @@ __device__ __forceinline__ void products(RD rd, MF mf) {
   }
 }
 
-// Direct global->LDS load of one 64-row tile (rows clamped to [0, N-1]); wave
-// w fills rows of its NLD wave-loads, chunk (lane % CH) of each.
+// Direct global->LDS load of one 64-row tile (rows clamped to [0, N-1]).
+// Wave-load j (j = wave * NLD + i) fills LDS rows RPL j .. RPL j + RPL - 1, lane
+// l writing stored chunk l % CH of row RPL j + l / CH, so it fetches the global
+// chunk that the swizzle puts there.  The swizzle reads only row bits 0-3, and
+// RPL * NLD = 16, so it splits into a lane part and a constant per i:
+// bswz(RPL j + lr) = bswz(lr) ^ bswz(RPL i) for lr < RPL.  A load then costs
+// four address instructions (add, clamp, xor, shift-add) instead of about
+// fifteen.
 template <int D>
 __device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char* dst, int wave, int lane) {
   using T = Tile<D, kBT>;
-  // the lane index through an empty asm: the per-lane addresses are recomputed
-  // at each tile instead of being held in registers across the loop
+  constexpr int RPL = 64 / T::CH;   // rows per wave-load
+  static_assert(RPL * T::NLD == 16, "a wave's loads span 16 rows, a whole period of the swizzle");
+  // the lane index through an empty asm: the per-lane parts are recomputed at
+  // each tile instead of being held in registers across the loop
   asm volatile("" : "+v"(lane));
+  const int lr = lane / T::CH;
+  const uint32_t lc = (uint32_t)(((lane % T::CH) ^ bswz<D>(lr)) << 4);
 #pragma unroll
   for (int i = 0; i < T::NLD; ++i) {
-    const int pos = (wave * T::NLD + i) * 64 + lane;
-    const int row = pos / T::CH;
-    const int cst = pos % T::CH;
-    const int r = min(r0 + row, N - 1);
-    dma16s(src, (uint32_t)(((size_t)r * D + ((cst ^ bswz<D>(row)) << 3)) * 2), dst + (wave * T::NLD + i) * 1024);
+    const int j = wave * T::NLD + i;
+    const int r = min(r0 + j * RPL + lr, N - 1);
+    dma16s(src, (uint32_t)r * (uint32_t)(D * 2) + (lc ^ (uint32_t)(bswz<D>(RPL * i) << 4)), dst + j * 1024);
   }
 }
 

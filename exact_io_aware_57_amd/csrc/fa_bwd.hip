@@ -28,6 +28,9 @@
 //     holds its 32 queries' Q and dO rows and dQ^T, and streams 64-key tiles of
 //     K and V:  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //     dQ^T += K^T dS^T.
+//     On grids of at least 256 workgroups of 256 queries, dQ runs in a
+//     ping-pong form instead (bwd_dq_pp_kernel): 8 waves in two groups that
+//     alternate the products with the exponentials, one phase apart.
 // Computing dQ in its own pass recomputes S and dP once more (7 products per
 // score instead of 5) in exchange for no atomic accumulation of dQ across key
 // tiles.
@@ -530,6 +533,275 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 3b. dQ, ping-pong form for large grids: 8 waves in two groups of 4 (waves w
+// and w + 4 share a SIMD), 256 queries per workgroup (32 per wave), BT-key
+// tiles (64 as launched; 32-key tiles measured slower).  Each wave alternates a matrix phase (dQ^T += K^T dS^T of tile t - 1,
+// then S^T and dP^T of tile t) with a VALU phase (P and dS of tile t); the two
+// groups run one phase apart, so on every SIMD one wave keeps the matrix core
+// busy while the other computes exponentials, as in the 8-wave forward kernel.
+// K has three LDS buffers (tile t - 1 is read transposed by the dQ product
+// while tile t is read as rows and tile t + 1 loads), V two.  At every even
+// phase 2t the workgroup issues the loads of tile t + 1 and waits for them at
+// the end of phase 2t + 1; the first reads of that tile come at phase 2t + 2,
+// and the buffers it overwrites were last read in phases 2t - 2 and 2t - 1.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, int BT>
+__global__ __launch_bounds__(512, 1) void bwd_dq_pp_kernel(BwdParams p) {
+  constexpr int KB = BT / 32;         // 32-key blocks per tile
+  constexpr int BM = 256;             // queries per workgroup
+  constexpr int ROW = D * 2;          // bytes per row
+  constexpr int MAT = BT * ROW;       // one K or V tile
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;        // rows per 1 KB wave-load
+  constexpr int NWL = MAT / 1024;     // wave-loads per matrix
+  constexpr int DC = D / 16, DB = D / 32;
+  static_assert(NWL % 8 == 0 || NWL == 4, "wave-loads split over 8 waves");
+  __shared__ __attribute__((aligned(1024))) char kbuf[3][MAT];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2][MAT];
+
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63;
+  const int r32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int ntiles = (N + BM - 1) / BM;
+  const int total = gridDim.x;
+  const int bid = blockIdx.x;
+  const int per = total >> 3;
+  const int lid = (bid < (per << 3)) ? (bid & 7) * per + (bid >> 3) : bid;
+  const int bh = lid / ntiles;
+  int qt = lid - bh * ntiles;
+  if (CAUSAL) qt = ntiles - 1 - qt;   // heaviest first
+  const int b = bh / p.H;
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + (bh - b * p.H) / (p.H / p.Hkv)) * (size_t)N * D;
+  const __bf16* Kh = uniform_ptr(reinterpret_cast<const __bf16*>(p.k) + kvoff);
+  const __bf16* Vh = uniform_ptr(reinterpret_cast<const __bf16*>(p.v) + kvoff);
+
+  int L = N;
+  if (p.seqlens) {
+    const int x = p.seqlens[b];
+    L = x < 0 ? 0 : (x > N ? N : x);
+  }
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + r32;
+  int kv_end = L;
+  if (CAUSAL) kv_end = min(kv_end, q0 + BM);
+  const int ntk = (kv_end + BT - 1) / BT;              // tiles the workgroup streams
+  int last = ntk - 1;                                   // last tile this wave needs
+  if (CAUSAL) last = min(last, (qw0 + 31) / BT);
+
+  bf16x8 qf[DC], gf[DC];
+  {
+    const int qr = min(qi, N - 1);
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.q) + hoff + (size_t)qr * D);
+    const u32x4* grow = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(p.dout) + hoff + (size_t)qr * D);
+#pragma unroll
+    for (int s = 0; s < DC; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, qrow[2 * s + hi]);
+      gf[s] = __builtin_bit_cast(bf16x8, grow[2 * s + hi]);
+    }
+  }
+  // rows past the padded end read the last padded row; their results are not stored
+  const float lse2 = p.lse2[(size_t)bh * p.Npad + min(qi, p.Npad - 1)];
+  const float dsum = p.delta[(size_t)bh * p.Npad + min(qi, p.Npad - 1)];
+
+  // Tile loads: wave-load j of a matrix fills rows RPL j .. RPL j + RPL - 1
+  // (the split of the swizzle as in load_tile: bswz(RPL j + lr) = bswz(lr) ^
+  // bswz(RPL j)).  Wave w issues K wave-load w and V wave-load w (d = 128), or
+  // K wave-load w (waves 0-3) or V wave-load w - 4 (waves 4-7, d = 64).
+  auto load_kv = [&](int t) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln / CH;
+    const uint32_t lc = (uint32_t)(((ln % CH) ^ bswz<D>(lr)) << 4);
+    auto one = [&](const __bf16* src, char* dst, int j) __attribute__((always_inline)) {
+      const int r = min(t * BT + j * RPL + lr, N - 1);
+      dma16s(src, (uint32_t)r * (uint32_t)ROW + (lc ^ (uint32_t)(bswz<D>(RPL * j) << 4)), dst + j * 1024);
+    };
+    if constexpr (NWL % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < NWL / 8; ++i) {
+        one(Kh, kbuf[t % 3], wave + 8 * i);
+        one(Vh, vbuf[t & 1], wave + 8 * i);
+      }
+    } else {
+      if (wave < 4)
+        one(Kh, kbuf[t % 3], wave);
+      else
+        one(Vh, vbuf[t & 1], wave - 4);
+    }
+  };
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int cb = 0; cb < DB; ++cb) dqacc[cb] = f32x16{};
+  f32x16 sacc[KB], pacc[KB];                  // S^T, dP^T of the tile in flight
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    sacc[kb] = f32x16{};
+    pacc[kb] = f32x16{};
+  }
+  uint32_t dk[KB][8] = {};                    // dS^T of the previous tile, bf16 pairs
+  const float sc = p.scale * kLog2e;
+  const TileAddr<D> ad(lane);
+
+  // Matrix phase: dQ^T += K_tq^T dS^T (if DO_DQ), then S^T and dP^T of tile ts
+  // (if DO_S), the S^T and dP^T products interleaved (two accumulation chains).
+  auto mfma_phase = [&](const bool DO_DQ, int tq, const bool DO_S, int ts) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    int rb = ad.row_base, tb0 = ad.tr_base0, tb1 = ad.tr_base1;
+    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+    if (DO_DQ) {
+      // product i: key block kb = i / (2 DB), half u = (i / DB) % 2, column block cb = i % DB
+      const char* Kq = kbuf[tq % 3];
+      products<2 * DB * KB, 2>(
+          [&](int i) __attribute__((always_inline)) { return read_tr<D>(Kq, tb0, tb1, i / (2 * DB), (i / DB) & 1, i % DB); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            const int kb = i / (2 * DB), u = (i / DB) & 1;
+            const bf16x8 bs = __builtin_bit_cast(bf16x8, u32x4{dk[kb][4 * u], dk[kb][4 * u + 1], dk[kb][4 * u + 2], dk[kb][4 * u + 3]});
+            dqacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bs, dqacc[i % DB], 0, 0, 0);
+          });
+    }
+    if (DO_S) {
+      // product i: chain c = i % (2 KB) (S^T of block c / 2, or dP^T of it if c is odd), k-step i / (2 KB)
+      const char* Ks = kbuf[ts % 3];
+      const char* Vs = vbuf[ts & 1];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        sacc[kb] = f32x16{};
+        pacc[kb] = f32x16{};
+      }
+      products<2 * DC * KB, 4>(
+          [&](int i) __attribute__((always_inline)) {
+            const int c = i % (2 * KB), st = i / (2 * KB);
+            return (c & 1) ? read_row<D>(Vs, rb, c >> 1, st) : read_row<D>(Ks, rb, c >> 1, st);
+          },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            const int c = i % (2 * KB), st = i / (2 * KB);
+            if (c & 1)
+              pacc[c >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[st], pacc[c >> 1], 0, 0, 0);
+            else
+              sacc[c >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], sacc[c >> 1], 0, 0, 0);
+          });
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pin(sacc[kb]);
+      pin(pacc[kb]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) pin(dqacc[cb]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // VALU phase: P = exp2(S scale log2e - lse2) (masked), dS = P (dP - D), packed.
+  // Register r holds key 32 t + 8 (r / 4) + 4 hi + r % 4 of this lane's query.
+  auto valu_phase = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * BT;
+    auto body = [&](const bool MASK) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float dsv[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * j + e;
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], sc, -lse2));
+            if (MASK) {
+              const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+              const bool ok = kk < L && (!CAUSAL || kk <= qi);
+              pr = ok ? pr : 0.0f;
+            }
+            dsv[e] = pr * (pacc[kb][r] - dsum);
+          }
+          dk[kb][j] = pack_bf16(dsv[0], dsv[1]);
+        }
+    };
+    const bool need_mask = (k0 + BT > L) || (CAUSAL && k0 + BT - 1 > qw0);
+    if (need_mask)
+      body(true);
+    else
+      body(false);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pin(dk[kb][j]);
+  };
+
+  // Global phase counter, identical in every wave (all waves meet every
+  // barrier, including waves past their last tile).
+  const int n_phases = 2 * ntk + 2;
+  int ph = 0;
+  auto begin_phase = [&]() __attribute__((always_inline)) {
+    if ((ph & 1) == 0) {
+      const int t = ph >> 1;
+      if (t + 1 < ntk) load_kv(t + 1);
+    }
+  };
+  auto end_phase = [&]() __attribute__((always_inline)) {
+    if (ph & 1) wait_vmem();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    ++ph;
+  };
+  if (ntk > 0) {
+    load_kv(0);
+    wait_vmem();
+    __syncthreads();
+    if (grp == 1) {   // the second group starts one phase late
+      begin_phase();
+      end_phase();
+    }
+    if (last >= 0) {
+      begin_phase();
+      mfma_phase(false, 0, true, 0);
+      end_phase();
+      for (int t = 0; t < last; ++t) {
+        begin_phase();
+        valu_phase(t);
+        end_phase();
+        begin_phase();
+        mfma_phase(true, t, true, t + 1);
+        end_phase();
+      }
+      begin_phase();
+      valu_phase(last);
+      end_phase();
+      begin_phase();
+      mfma_phase(true, last, false, 0);
+      end_phase();
+    }
+    while (ph < n_phases) {   // keep loading and meeting the barriers
+      begin_phase();
+      end_phase();
+    }
+  }
+
+  if (qi < N) {
+    __bf16* orow = reinterpret_cast<__bf16*>(p.dq) + hoff + (size_t)qi * D;
+#pragma unroll
+    for (int cb = 0; cb < DB; ++cb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int col = cb * 32 + 8 * gq + 4 * hi;
+        const u32x2 w = {pack_bf16(dqacc[cb][4 * gq] * p.scale, dqacc[cb][4 * gq + 1] * p.scale),
+                         pack_bf16(dqacc[cb][4 * gq + 2] * p.scale, dqacc[cb][4 * gq + 3] * p.scale)};
+        *reinterpret_cast<u32x2*>(orow + col) = w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   BwdParams arg = p;
@@ -543,6 +815,15 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
                             : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, false>);
   e = hipLaunchKernel(kv, dim3(nt * (unsigned)p.B * (unsigned)p.Hkv), dim3(kThreads), args, 0, stream);
   if (e != hipSuccess) return e;
+  // dQ: the ping-pong form once its grid (256 queries per workgroup) fills the
+  // chip, else the 4-wave form with two workgroups per compute unit.  Both
+  // sum every dQ row over 32-key blocks in the same order (bitwise equal).
+  const unsigned ntp = (unsigned)((p.N + 255) / 256);
+  if (ntp * (unsigned)p.B * (unsigned)p.H >= 256u) {
+    const void* dqp = p.causal ? reinterpret_cast<const void*>(&bwd_dq_pp_kernel<D, true, 64>)
+                               : reinterpret_cast<const void*>(&bwd_dq_pp_kernel<D, false, 64>);
+    return hipLaunchKernel(dqp, dim3(ntp * (unsigned)p.B * (unsigned)p.H), dim3(512), args, 0, stream);
+  }
   const void* dq = p.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, true>)
                             : reinterpret_cast<const void*>(&bwd_dq_kernel<D, false>);
   return hipLaunchKernel(dq, dim3(nt * (unsigned)p.B * (unsigned)p.H), dim3(kThreads), args, 0, stream);

@@ -160,6 +160,16 @@ def test_backward_end_to_end(d, causal):
     check(q, k, v, do, 1.0 / math.sqrt(d), causal, sl, f"end to end d={d}", end_to_end=True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_large_grid(d, causal):
+    """At least 256 workgroups of 256 queries (B = 4, H = 16, five query tiles
+    of 256 per head), so dQ runs in the 8-wave ping-pong form: grouped heads,
+    per-batch lengths from 1 to N and a ragged last tile of 76 queries."""
+    q, k, v, do, sl = inputs(4, 16, 4, 1100, d, 400 + d + int(causal), (1, 1100))
+    check(q, k, v, do, 1.0 / math.sqrt(d), causal, sl, f"large grid d={d}")
+
+
 def test_backward_long_sequence():
     """A few thousand keys: many query tiles per key tile, every key tile of a
     head in flight."""

@@ -170,6 +170,17 @@ def test_backward_large_grid(d, causal):
     check(q, k, v, do, 1.0 / math.sqrt(d), causal, sl, f"large grid d={d}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_large_grid_padding(causal):
+    """The ping-pong dQ path with an empty batch, a one-key batch and a full
+    one: the empty batch gets no gradient, keys past a length get none."""
+    q, k, v, do, _ = inputs(4, 16, 8, 1100, 128, 650 + int(causal))
+    sl = torch.tensor([0, 1, 700, 1100], dtype=torch.int32)
+    dq, dk, dv = check(q, k, v, do, 0.0884, causal, sl, "large grid padding")
+    assert torch.all(dq[0] == 0) and torch.all(dk[0] == 0) and torch.all(dv[0] == 0)
+    assert torch.all(dk[1, :, 1:] == 0) and torch.all(dv[2, :, 700:] == 0)
+
+
 def test_backward_long_sequence():
     """A few thousand keys: many query tiles per key tile, every key tile of a
     head in flight."""

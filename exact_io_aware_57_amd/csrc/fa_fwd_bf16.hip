@@ -879,7 +879,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
   constexpr bool kEvenBarrier = D < 128;
   const int n_phases = 2 * ntk + 2;
   int ph = 0;
-  auto begin_phase = [&]() __attribute__((always_inline)) {
+  auto issue_tile = [&]() __attribute__((always_inline)) {
     if ((ph & 1) == 0) {
       const int t = ph >> 1;
       if (t < ntk) {
@@ -887,6 +887,22 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
         load_v(t);
       }
     }
+  };
+  // At head size 128 and 256 the wave entering its matrix phase issues its
+  // share of an even phase's loads after its products, not before them: the
+  // issue then no longer delays the tile's first products, while the other
+  // group, entering its softmax phase, still issues at the start (long context
+  // 1.823 -> 1.811 ms, d = 256 1.837 -> 1.790 ms, non-causal d = 128
+  // 0.890 -> 0.883 ms; results bitwise equal).  Issuing between the products
+  // measured the same.  The loads still precede the wait at the end of the
+  // next phase, and the buffers they fill were last read before the barrier
+  // that ends the phase before.
+  constexpr bool kLateMatrixIssue = D >= 128;
+  auto begin_phase = [&](const bool matrix_next = false) __attribute__((always_inline)) {
+    if (!(kLateMatrixIssue && matrix_next)) issue_tile();
+  };
+  auto after_matrix = [&]() __attribute__((always_inline)) {
+    if (kLateMatrixIssue) issue_tile();
   };
   auto end_phase = [&]() __attribute__((always_inline)) {
     if (ph & 1) wait_vmem();
@@ -904,22 +920,25 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_pp_kernel(FwdParams p) {
       end_phase();
     }
     if (last >= 0) {
-      begin_phase();
+      begin_phase(true);
       mfma_phase(false, 0, true, 0);
+      after_matrix();
       end_phase();
       for (int t = 0; t < last; ++t) {
         begin_phase();
         softmax(t);
         end_phase();
-        begin_phase();
+        begin_phase(true);
         mfma_phase(true, t, true, t + 1);
+        after_matrix();
         end_phase();
       }
       begin_phase();
       softmax(last);
       end_phase();
-      begin_phase();
+      begin_phase(true);
       mfma_phase(true, last, false, 0);
+      after_matrix();
       end_phase();
     }
     while (ph < n_phases) {      // keep loading and meeting the barriers

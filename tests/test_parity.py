@@ -235,6 +235,24 @@ def test_large_grid_full_heads_ragged(d, causal):
                          f"large grid full heads N={N} d={d}")
 
 
+# Shapes on both sides of each kernel-choice threshold of the bf16 forward
+# pass (grid size G in workgroups of 256 query rows, key range N): every row
+# of the first, a middle and the last head against the oracle.
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 32, 1024, 128, False), (1, 33, 1024, 128, False),    # G = 128 (two key groups) | 132 (8-wave)
+    (1, 32, 1024, 128, True), (1, 33, 1024, 128, True),
+    (1, 64, 1023, 128, False), (1, 48, 767, 128, True),      # under 1024 keys: 4-wave; 767 keys, small grid
+    (1, 64, 2048, 64, False), (1, 31, 2048, 64, False),      # G = 512 (8-wave) | 248 (4-wave)
+    (1, 64, 2047, 64, False),                                # 2047 keys: 4-wave
+    (1, 32, 4096, 64, True), (1, 32, 4095, 64, True),        # causal d = 64 from 4096 keys
+    (1, 32, 2048, 256, True), (1, 31, 2048, 256, True),      # G = 256 (8-wave) | 248 (head-size-256 kernel)
+])
+def test_kernel_choice_thresholds(B, H, N, d, causal):
+    q, k, v, _ = random_qkv(B, H, N, d, torch.bfloat16, 1.0, seed=7 * N + H + d + int(causal))
+    check_full_heads(q, k, v, 1.0 / math.sqrt(d), causal, None, [(0, 0), (0, H // 2), (B - 1, H - 1)],
+                     f"threshold B={B} H={H} N={N} d={d}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_grid_full_heads_long_keys_d64(causal):
     # head size 64 with at least 2048 keys: 128-key tiles, in the 8-wave kernel

@@ -34,9 +34,8 @@ DEVICE_FLAGS = [
 # AGPR-resident accumulators would cost a v_accvgpr move per element.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # Sources whose kernels run one wave per SIMD and need the accumulation
-# registers as well (head size 256: 64 registers of Q and 128 of O^T per lane;
-# the backward kernels: two transposed gradient accumulators per wave).
-AGPR_FORM_SOURCES = {"fa_fwd_bf16_d256.hip", "fa_bwd.hip"}
+# registers as well (head size 256: 64 registers of Q and 128 of O^T per lane).
+AGPR_FORM_SOURCES = {"fa_fwd_bf16_d256.hip"}
 
 
 def device_flags(src):

@@ -39,9 +39,9 @@
 // operand of S, dP) and transposed (A operand of dK^T, dV^T, dQ^T, via
 // ds_read_b64_tr_b16), so their 16-byte chunks are stored with one XOR
 // swizzle that keeps both access patterns free of bank conflicts.
-// The dK/dV kernel runs one wave per SIMD and keeps its accumulators in the
-// accumulation registers (this source is compiled without the VGPR-form
-// option); the dQ kernel fits two waves per SIMD in 256 registers.
+// The dK/dV kernel runs one wave per SIMD: its 256 VGPRs hold the operands and
+// the gradient accumulators, with a few values parked in the accumulation
+// registers; the dQ kernels fit two waves per SIMD in 256 registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -166,21 +166,32 @@ __device__ __forceinline__ void products(RD rd, MF mf) {
 // four address instructions (add, clamp, xor, shift-add) instead of about
 // fifteen.
 template <int D>
-__device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char* dst, int wave, int lane) {
+struct LoadLane {
   using T = Tile<D, kBT>;
-  constexpr int RPL = 64 / T::CH;   // rows per wave-load
+  static constexpr int RPL = 64 / T::CH;   // rows per wave-load
   static_assert(RPL * T::NLD == 16, "a wave's loads span 16 rows, a whole period of the swizzle");
+  int lr;        // row within a wave-load
+  uint32_t lc;   // byte offset of the lane's chunk before the per-load constant
   // the lane index through an empty asm: the per-lane parts are recomputed at
   // each tile instead of being held in registers across the loop
-  asm volatile("" : "+v"(lane));
-  const int lr = lane / T::CH;
-  const uint32_t lc = (uint32_t)(((lane % T::CH) ^ bswz<D>(lr)) << 4);
-#pragma unroll
-  for (int i = 0; i < T::NLD; ++i) {
+  __device__ __forceinline__ explicit LoadLane(int lane) {
+    asm volatile("" : "+v"(lane));
+    lr = lane / T::CH;
+    lc = (uint32_t)(((lane % T::CH) ^ bswz<D>(lr)) << 4);
+  }
+  // wave-load i of this wave's part of the tile at rows r0 .. r0 + 63
+  __device__ __forceinline__ void load(const __bf16* src, int r0, int N, char* dst, int wave, int i) const {
     const int j = wave * T::NLD + i;
     const int r = min(r0 + j * RPL + lr, N - 1);
     dma16s(src, (uint32_t)r * (uint32_t)(D * 2) + (lc ^ (uint32_t)(bswz<D>(RPL * i) << 4)), dst + j * 1024);
   }
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(const __bf16* src, int r0, int N, char* dst, int wave, int lane) {
+  const LoadLane<D> ll(lane);
+#pragma unroll
+  for (int i = 0; i < Tile<D, kBT>::NLD; ++i) ll.load(src, r0, N, dst, wave, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,8 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int DC = T::DC, DB = T::DB;
   constexpr int QMAT = 2 * T::MAT;                  // one 128-row tile of Q or dO
   constexpr int STAGE = 2 * QMAT + 2 * kQT * 4;      // Q, dO, lse2[128], D[128]
-  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  static_assert(STAGE % 1024 == 0, "a stage offset leaves the swizzled low address bits alone");
+  __shared__ __attribute__((aligned(1024))) char stages[2 * STAGE];
 
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -265,13 +276,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float sc = p.scale * kLog2e;
   const TileAddr<D> ad(lane);
 
-  auto tile = [&](const bool MASK, const char* st, int q0) __attribute__((always_inline)) {
-    const char* Qs = st;
-    const char* Gs = st + QMAT;
-    const float* ls = reinterpret_cast<const float*>(st + 2 * QMAT);
-    const float* ds = ls + kQT;
-    int rb = ad.row_base, tb0 = ad.tr_base0, tb1 = ad.tr_base1;
-    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1));
+  // One 128-query tile from the stage at byte offset soff.  The offset goes into
+  // the lane bases (opaque, so each is one register per tile); lse2 and D of
+  // query qo sit at stages + lb + 4 qo and + 4 (kQT + qo), the lane part 16 hi
+  // in lb.  spread(c, i) issues wave-load i of chunk c of the next tile.
+  auto tile = [&](const bool mask, const int soff, int q0, auto&& spread) __attribute__((always_inline)) {
+    const char* Qs = stages;
+    const char* Gs = stages + QMAT;
+    int rb = ad.row_base + soff, tb0 = ad.tr_base0 + soff, tb1 = ad.tr_base1 + soff, lb = 2 * QMAT + 16 * hi + soff;
+    asm volatile("" : "+v"(rb), "+v"(tb0), "+v"(tb1), "+v"(lb));
 #pragma unroll
     for (int qb = 0; qb < kQT / 32; ++qb) {
       // S[q][key] = Q K^T and dP[q][key] = dO V^T for 32 queries
@@ -283,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
               sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[i], sacc, 0, 0, 0);
             else
               pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[i - DC], pacc, 0, 0, 0);
+            if (i < T::NLD) spread(qb, i);
           });
       // register r holds query q0 + 32 qb + 8 (r / 4) + 4 hi + r % 4
       uint32_t pk[8], dk[8];
@@ -290,20 +304,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       for (int gq = 0; gq < 4; ++gq) {
         typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
         const int qo = qb * 32 + 8 * gq + 4 * hi;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + qo);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(stages + lb + 4 * (qb * 32 + 8 * gq));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(stages + lb + 4 * (kQT + qb * 32 + 8 * gq));
         float pv[4], dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * gq + e], sc, -l4[e]));
-          if (MASK) {
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * gq + e], sc, -l4[e]));
+        if (mask) {   // wave-uniform: only tiles on the diagonal or at a ragged end
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
             const int q = q0 + qo + e;
             const bool ok = q < N && key < L && (!CAUSAL || key <= q);
-            pr = ok ? pr : 0.0f;
+            pv[e] = ok ? pv[e] : 0.0f;
           }
-          pv[e] = pr;
-          dsv[e] = pr * (pacc[4 * gq + e] - d4[e]);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[e] = pv[e] * (pacc[4 * gq + e] - d4[e]);
         pk[2 * gq] = pack_bf16(pv[0], pv[1]);
         pk[2 * gq + 1] = pack_bf16(pv[2], pv[3]);
         dk[2 * gq] = pack_bf16(dsv[0], dsv[1]);
@@ -332,27 +347,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  auto step = [&](int it, const char* cur, char* next) __attribute__((always_inline)) {
-    if (it + 1 < n_it) issue_loads(it + 1, next);
+  // Every wave with a valid key works on every tile: the first query tile of a
+  // causal workgroup starts at the workgroup's first key, so it reaches every
+  // wave's keys.  Waves whose keys all lie at or past L only load.  One code
+  // path per tile (the mask a wave-uniform branch inside it, the stage an
+  // offset) keeps the accumulators in the same registers from tile to tile.
+  static_assert(kQT == kRowsWG, "query tiles start at the workgroup's first key");
+  static_assert(kQT / 32 == 4, "four 32-query blocks issue the four 64-row chunks of the next tile");
+  auto step = [&](int it) __attribute__((always_inline)) {
+    const bool more = it + 1 < n_it;
+    const int soff = (it & 1) * STAGE;
+    char* next = stages + (STAGE - soff);
     const int q0 = (qstart + it % per_head) * kQT;
-    const bool active = wave_live && (!CAUSAL || q0 + kQT - 1 >= kw0);
-    if (active) {
-      const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
-      if (need_mask)
-        tile(true, cur, q0);
-      else
-        tile(false, cur, q0);
+    // The next tile's loads are spread over this tile's four 32-query blocks:
+    // block c issues chunk c (Q rows 0-63, Q rows 64-127, dO rows 0-63, dO rows
+    // 64-127), one wave-load after each of its first NLD products, so that the
+    // loads queue beside the products instead of stalling the wave at once.
+    const int itn = more ? it + 1 : it;
+    const int hqn = g * G + itn / per_head;
+    const int q0n = (qstart + itn % per_head) * kQT;
+    const size_t hoffn = ((size_t)b * p.H + hqn) * (size_t)N * D;
+    const __bf16* qsrc = reinterpret_cast<const __bf16*>(p.q) + hoffn;
+    const __bf16* gsrc = reinterpret_cast<const __bf16*>(p.dout) + hoffn;
+    const LoadLane<D> ll(lane);
+    if (more && wave < 2 && lane < 32) {   // 128 floats of lse2 (wave 0) or D (wave 1)
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + hqn) * (size_t)p.Npad + q0n;
+      dma16s(src, (uint32_t)(lane * 16), next + 2 * QMAT + wave * kQT * 4);
     }
+    auto spread = [&](int c, int i) __attribute__((always_inline)) {
+      if (more) ll.load(c < 2 ? qsrc : gsrc, q0n + (c & 1) * kBT, N, next + (c >> 1) * QMAT + (c & 1) * T::MAT, wave, i);
+    };
+    const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > L) || (CAUSAL && q0 < kw0 + 31);
+    tile(need_mask, soff, q0, spread);
     wait_vmem();
     __syncthreads();
   };
 
-  if (n_it > 0) issue_loads(0, stage0);
+  if (n_it > 0) issue_loads(0, stages);
   wait_vmem();
   __syncthreads();
-  for (int it = 0; it < n_it; it += 2) {
-    step(it, stage0, stage1);
-    if (it + 1 < n_it) step(it + 1, stage1, stage0);
+  if (wave_live) {
+    for (int it = 0; it < n_it; ++it) step(it);
+  } else {
+    for (int it = 0; it < n_it; ++it) {   // the same barriers, loads only
+      if (it + 1 < n_it) issue_loads(it + 1, stages + ((it + 1) & 1) * STAGE);
+      wait_vmem();
+      __syncthreads();
+    }
   }
 
   // dV^T, dK^T register r: column 32 cb + 8 (r / 4) + 4 hi + r % 4 of this lane's key

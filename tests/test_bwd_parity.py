@@ -261,3 +261,26 @@ def test_backward_long_context_full_size():
         rel = np.linalg.norm(err) / np.linalg.norm(ref)
         say(f"[bwd] long context head {h} sampled dQ rows: max err {err.max():.3e} normwise rel {rel:.3e}")
         assert rel <= 2.0 ** -6
+
+
+def test_backward_random_shapes():
+    """Twelve shapes drawn from a fixed seed: head sizes 64 and 128, grouped
+    heads, causal or not, key-padding lengths including zero, and grids on both
+    sides of the ping-pong dQ threshold (ceil(N / 256) * B * H >= 256)."""
+    import random
+    rng = random.Random(7)
+    for c in range(12):
+        d = rng.choice([64, 128])
+        H_kv, G = rng.choice([1, 2, 4]), rng.choice([1, 2, 4])
+        if c % 3 == 0:
+            B, H, N = rng.choice([2, 4]), 16, rng.randint(600, 1300)
+            H_kv = 16 // G
+        else:
+            B, H, N = rng.choice([1, 2, 3]), H_kv * G, rng.randint(1, 700)
+        causal = rng.random() < 0.5
+        use_len = rng.random() < 0.5
+        seed = rng.randint(0, 10 ** 6)
+        q, k, v, do, sl = inputs(B, H, H_kv, N, d, seed, (0, N) if use_len else None)
+        if use_len:
+            sl[rng.randrange(B)] = 0
+        check(q, k, v, do, 1.0 / math.sqrt(d), causal, sl, f"random {c}: B{B} H{H}/{H_kv} N{N} d{d} causal={causal}")
